@@ -1,0 +1,222 @@
+// ds4hc_api.cpp -- the C ABI declared in include/ds4hc.h: host-side argument
+// validation, choice between the row-resident and split-K paths, and launch.
+//
+// Nothing here touches the GPU until every argument has been checked, so all
+// rejections are free of side effects. The library holds no device memory:
+// per-device scratch is the caller's workspace argument. (lucebox PR #507
+// "correct layer-split HC handoff and per-device state" fixed a bug where an
+// HC scratch buffer was shared across devices; a library without global
+// scratch cannot have it.)
+#include "ds4hc.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "hc_launch.hpp"
+
+namespace {
+
+constexpr int64_t SPLITK_MAX_T = 32;       // T at or below which split-K is the default
+constexpr int64_t MAX_T = int64_t(1) << 24;
+constexpr int MAX_ITERS = 1000;
+constexpr uint64_t MAX_WORK_ITEMS = 0xFFFFFFFFull;  // HSA dispatch grid size is 32-bit
+constexpr uint32_t KNOWN_FLAGS =
+    DS4HC_FLAG_DETERMINISTIC | DS4HC_FLAG_FORCE_ROWRES | DS4HC_FLAG_FORCE_SPLITK;
+
+thread_local char g_last_hip_error[256] = "";
+
+ds4hc_status hip_fail(hipError_t e) {
+    snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return DS4HC_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+    const void *p;
+    uint64_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+int state_bytes(ds4hc_dtype dt) { return dt == DS4HC_F32 ? 4 : 2; }
+int vec_elems(ds4hc_dtype dt) { return dt == DS4HC_F32 ? 4 : 8; }
+
+// Checks shared by pre / post / fused on the op constants.
+ds4hc_status check_params(const ds4hc_params *p, int64_t T, ds4hc_dtype dt) {
+    if (!p) return DS4HC_ERR_INVALID_ARG;
+    if (dt != DS4HC_F32 && dt != DS4HC_BF16) return DS4HC_ERR_INVALID_ARG;
+    if (T < 0 || p->n_hc < 1 || p->d <= 0 || p->d % 8 != 0) return DS4HC_ERR_INVALID_ARG;
+    if (!(p->rms_eps >= 0.f) || !isfinite(p->rms_eps)) return DS4HC_ERR_INVALID_ARG;
+    if (p->sinkhorn_iters < 0) return DS4HC_ERR_INVALID_ARG;
+    if (p->flags & ~KNOWN_FLAGS) return DS4HC_ERR_INVALID_ARG;
+    if ((p->flags & DS4HC_FLAG_FORCE_ROWRES) && (p->flags & DS4HC_FLAG_FORCE_SPLITK))
+        return DS4HC_ERR_INVALID_ARG;
+    if (p->n_hc != 1 && p->n_hc != 2 && p->n_hc != 4) return DS4HC_ERR_UNSUPPORTED;
+    if (p->sinkhorn_iters > MAX_ITERS || T > MAX_T) return DS4HC_ERR_UNSUPPORTED;
+    return DS4HC_OK;
+}
+
+struct Plan {
+    bool rowres;
+    int P;                 // split-K chunks
+    uint64_t ws_bytes;     // workspace needed
+};
+
+// Path for HC-pre / fused. Returns UNSUPPORTED if a launch would not fit.
+ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *out) {
+    const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
+    const int cq = ds4hc::rowres_chunks(d, dt);
+    const bool fits_rowres = cq <= ds4hc::rowres_max_chunks(n, dt);
+    bool rowres;
+    if (p->flags & DS4HC_FLAG_FORCE_ROWRES) {
+        if (!fits_rowres) return DS4HC_ERR_UNSUPPORTED;
+        rowres = true;
+    } else if (p->flags & DS4HC_FLAG_FORCE_SPLITK) {
+        rowres = false;
+    } else {
+        rowres = fits_rowres && T > SPLITK_MAX_T;
+    }
+    Plan pl{rowres, 0, 0};
+    if (rowres) {
+        if ((uint64_t)T * 256u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
+    } else {
+        pl.P = ds4hc::splitk_chunks(n, d, dt);
+        const uint64_t tg = (uint64_t)(T + 3) / 4;
+        const uint64_t cb = (uint64_t)(d + 64 * vec_elems(dt) - 1) / (64 * vec_elems(dt));
+        // partials grid (token groups, P), finish grid (T, column blocks)
+        if (tg * 64u > MAX_WORK_ITEMS || pl.P > 0xFFFF || (uint64_t)T * 64u > MAX_WORK_ITEMS ||
+            cb > 0xFFFFu)
+            return DS4HC_ERR_UNSUPPORTED;
+        pl.ws_bytes = (uint64_t)pl.P * (uint64_t)T * (uint64_t)(m + 1) * sizeof(float);
+    }
+    *out = pl;
+    return DS4HC_OK;
+}
+
+ds4hc_status run_hc(bool fused, const ds4hc_params *p, int64_t T, ds4hc_dtype dt, const void *X,
+                    const uint16_t *W, const float *bias, const void *layer_out, void *layer_in,
+                    float *coeffs, float *logits, void *X_out, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+    ds4hc_status st = check_params(p, T, dt);
+    if (st != DS4HC_OK || T == 0) return st;  // zero tokens: nothing is read or written
+    if (!X || !W || !bias || !layer_in) return DS4HC_ERR_INVALID_ARG;
+    if (!fused && !coeffs) return DS4HC_ERR_INVALID_ARG;
+    if (fused && (!layer_out || !X_out)) return DS4HC_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(W, 16) || !aligned(layer_in, 16) || !aligned(bias, 4) ||
+        (coeffs && !aligned(coeffs, 4)) || (logits && !aligned(logits, 4)) ||
+        (fused && (!aligned(layer_out, 16) || !aligned(X_out, 16))) ||
+        (workspace && !aligned(workspace, 4)))
+        return DS4HC_ERR_INVALID_ARG;
+
+    Plan pl;
+    st = make_plan(p, T, dt, &pl);
+    if (st != DS4HC_OK) return st;
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes))
+        return DS4HC_ERR_INVALID_ARG;
+
+    const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
+    const uint64_t sb = (uint64_t)state_bytes(dt), K = (uint64_t)n * d, uT = (uint64_t)T;
+    const Range rX{X, uT * K * sb}, rW{W, (uint64_t)m * K * 2}, rb{bias, (uint64_t)m * 4};
+    const Range rlo{fused ? layer_out : nullptr, uT * d * sb};
+    const Range rli{layer_in, uT * d * sb}, rc{coeffs, uT * m * 4}, rz{logits, uT * m * 4};
+    const Range rXo{fused ? X_out : nullptr, uT * K * sb};
+    const Range rws{pl.ws_bytes ? workspace : nullptr, pl.ws_bytes};
+    // Outputs must not overlap any other buffer, except that X_out may be exactly X.
+    const Range all[] = {rX, rW, rb, rlo, rli, rc, rz, rXo, rws};
+    constexpr int FIRST_OUT = 4, N_ALL = 9;
+    for (int a = FIRST_OUT; a < N_ALL; ++a) {
+        for (int b = 0; b < N_ALL; ++b) {
+            if (a == b) continue;
+            const bool in_place = (a == 7 && b == 0) && X_out == X;
+            if (!in_place && overlap(all[a], all[b])) return DS4HC_ERR_INVALID_ARG;
+        }
+    }
+
+    ds4hc::FusedArgs a{n, d, (int)dt, p->sinkhorn_iters, T, p->rms_eps, X, W, bias, layer_out,
+                       layer_in, coeffs, logits, X_out, static_cast<float *>(workspace)};
+    const hipError_t e = ds4hc::launch_hc(a, fused, pl.rowres, stream);
+    return e == hipSuccess ? DS4HC_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+ds4hc_status ds4hc_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                       const uint16_t *W_f16, const float *bias, void *layer_in, float *coeffs,
+                       float *logits_opt, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    return run_hc(false, p, T, dtype, X, W_f16, bias, nullptr, layer_in, coeffs, logits_opt,
+                  nullptr, workspace, workspace_bytes, stream);
+}
+
+ds4hc_status ds4hc_fused(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                         const uint16_t *W_f16, const float *bias, const void *layer_out,
+                         void *layer_in, float *coeffs_opt, void *X_out, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    return run_hc(true, p, T, dtype, X, W_f16, bias, layer_out, layer_in, coeffs_opt, nullptr,
+                  X_out, workspace, workspace_bytes, stream);
+}
+
+ds4hc_status ds4hc_post(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                        const float *coeffs, const void *layer_out, void *X_out,
+                        hipStream_t stream) {
+    ds4hc_status st = check_params(p, T, dtype);
+    if (st != DS4HC_OK || T == 0) return st;
+    if (!X || !coeffs || !layer_out || !X_out) return DS4HC_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(layer_out, 16) || !aligned(X_out, 16) || !aligned(coeffs, 4))
+        return DS4HC_ERR_INVALID_ARG;
+    const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
+    const uint64_t sb = (uint64_t)state_bytes(dtype), uT = (uint64_t)T, K = (uint64_t)n * d;
+    const Range rXo{X_out, uT * K * sb};
+    if (X_out != X && overlap(rXo, Range{X, uT * K * sb})) return DS4HC_ERR_INVALID_ARG;
+    if (overlap(rXo, Range{coeffs, uT * m * 4}) || overlap(rXo, Range{layer_out, uT * d * sb}))
+        return DS4HC_ERR_INVALID_ARG;
+    const uint64_t cb = (uint64_t)(d + 64 * vec_elems(dtype) - 1) / (64 * vec_elems(dtype));
+    if (cb > 0xFFFFu || uT * 64u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;  // grid (T, cb)
+    const hipError_t e = ds4hc::launch_post(n, (int)dtype, d, T, X, coeffs, layer_out, X_out, stream);
+    return e == hipSuccess ? DS4HC_OK : hip_fail(e);
+}
+
+ds4hc_status ds4hc_sinkhorn(int64_t T, int32_t n_hc, int32_t iters, const float *logits_res,
+                            float *H, hipStream_t stream) {
+    if (T < 0 || n_hc < 1 || iters < 0) return DS4HC_ERR_INVALID_ARG;
+    if (n_hc != 1 && n_hc != 2 && n_hc != 4) return DS4HC_ERR_UNSUPPORTED;
+    if (iters > MAX_ITERS || T > MAX_T) return DS4HC_ERR_UNSUPPORTED;
+    if (T == 0) return DS4HC_OK;
+    if (!logits_res || !H || !aligned(logits_res, 4) || !aligned(H, 4)) return DS4HC_ERR_INVALID_ARG;
+    const uint64_t bytes = (uint64_t)T * n_hc * n_hc * 4;
+    if (overlap(Range{logits_res, bytes}, Range{H, bytes})) return DS4HC_ERR_INVALID_ARG;
+    const hipError_t e = ds4hc::launch_sinkhorn(n_hc, iters, T, logits_res, H, stream);
+    return e == hipSuccess ? DS4HC_OK : hip_fail(e);
+}
+
+size_t ds4hc_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype) {
+    if (check_params(p, T, dtype) != DS4HC_OK) return 0;
+    Plan pl;
+    if (make_plan(p, T, dtype, &pl) != DS4HC_OK) return 0;
+    return (size_t)pl.ws_bytes;
+}
+
+const char *ds4hc_status_string(ds4hc_status s) {
+    switch (s) {
+    case DS4HC_OK: return "DS4HC_OK";
+    case DS4HC_ERR_INVALID_ARG: return "DS4HC_ERR_INVALID_ARG";
+    case DS4HC_ERR_UNSUPPORTED: return "DS4HC_ERR_UNSUPPORTED";
+    case DS4HC_ERR_HIP: return "DS4HC_ERR_HIP";
+    }
+    return "DS4HC_UNKNOWN_STATUS";
+}
+
+const char *ds4hc_last_hip_error(void) { return g_last_hip_error; }
+
+int ds4hc_abi_version(void) { return DS4HC_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,157 @@
+// hc_device.hpp -- device-side building blocks of the HC op for gfx950
+// (wave64). Storage types, 16-byte vector loads/stores, wavefront
+// reductions and the register-resident Sinkhorn.
+//
+// The Sinkhorn follows the design point of lucebox-hub PR #494 "fix(ds4):
+// keep ROCmFPX generation byte-safe" (comment on the Sinkhorn kernel
+// specialised for NHC = 4): the generic kernel spilled its matrix to scratch
+// memory (95 us per launch), the unrolled NHC = 4 kernel kept it in registers
+// (5.3 us). Here one lane holds one matrix entry, so the whole n x n matrix
+// lives in n*n lanes of a wavefront and row/column sums are lane shuffles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds4hc {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };
+
+constexpr int n_logits(int n) { return 2 * n + n * n; }
+
+// One 16-byte vector of state elements: 4 float32 or 8 bfloat16.
+template <int DT> struct StateVec;
+template <> struct StateVec<DT_F32> {
+    static constexpr int V = 4;
+    float4 raw;
+};
+template <> struct StateVec<DT_BF16> {
+    static constexpr int V = 8;
+    uint4 raw;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+}
+
+template <int DT>
+__device__ __forceinline__ StateVec<DT> load_vec(const void *base, size_t elem_off) {
+    StateVec<DT> v;
+    if constexpr (DT == DT_F32)
+        v.raw = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem_off);
+    else
+        v.raw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem_off);
+    return v;
+}
+
+template <int DT>
+__device__ __forceinline__ StateVec<DT> zero_vec() {
+    StateVec<DT> v;
+    if constexpr (DT == DT_F32)
+        v.raw = make_float4(0.f, 0.f, 0.f, 0.f);
+    else
+        v.raw = make_uint4(0u, 0u, 0u, 0u);
+    return v;
+}
+
+// Element e of a vector, widened to float32 (exact).
+template <int DT>
+__device__ __forceinline__ float vec_get(const StateVec<DT> &v, int e) {
+    if constexpr (DT == DT_F32) {
+        return e == 0 ? v.raw.x : e == 1 ? v.raw.y : e == 2 ? v.raw.z : v.raw.w;
+    } else {
+        const uint32_t w = e < 2 ? v.raw.x : e < 4 ? v.raw.y : e < 6 ? v.raw.z : v.raw.w;
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+}
+
+// Store V float32 values as one 16-byte vector of the state type (one RNE rounding).
+template <int DT>
+__device__ __forceinline__ void store_vec(void *base, size_t elem_off, const float *f) {
+    if constexpr (DT == DT_F32) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(base) + elem_off) =
+            make_float4(f[0], f[1], f[2], f[3]);
+    } else {
+        uint4 u;
+        u.x = f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16);
+        u.y = f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16);
+        u.z = f32_to_bf16_bits(f[4]) | (f32_to_bf16_bits(f[5]) << 16);
+        u.w = f32_to_bf16_bits(f[6]) | (f32_to_bf16_bits(f[7]) << 16);
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + elem_off) = u;
+    }
+}
+
+// W row slice of V float16 values (8 or 16 bytes), kept packed.
+template <int V> struct HalfVec;
+template <> struct HalfVec<4> { uint2 raw; };
+template <> struct HalfVec<8> { uint4 raw; };
+
+template <int V>
+__device__ __forceinline__ HalfVec<V> load_half_vec(const uint16_t *p) {
+    HalfVec<V> h;
+    if constexpr (V == 4)
+        h.raw = *reinterpret_cast<const uint2 *>(p);
+    else
+        h.raw = *reinterpret_cast<const uint4 *>(p);
+    return h;
+}
+
+template <int V>
+__device__ __forceinline__ float half_get(const HalfVec<V> &h, int e) {
+    uint32_t w;
+    if constexpr (V == 4)
+        w = e < 2 ? h.raw.x : h.raw.y;
+    else
+        w = e < 2 ? h.raw.x : e < 4 ? h.raw.y : e < 6 ? h.raw.z : h.raw.w;
+    return (e & 1) ? f16_hi(w) : f16_lo(w);
+}
+
+// Sum over the 64 lanes of a wavefront by xor butterfly. Every lane ends with
+// the same bits: each step adds two identical pairs in commutative order.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1)
+        v += __shfl_xor(v, s, 64);
+    return v;
+}
+
+// Register-resident Sinkhorn. Lanes form groups of N*N; lane l of a group
+// holds Z[i][j] with i = (l % N^2) / N, j = l % N. All 64 lanes must call it.
+// Returns H[i][j] after: M = exp(Z - rowmax Z), then `iters` x (divide by row
+// sums, then by column sums).
+template <int N>
+__device__ __forceinline__ float sinkhorn_lane(float z, int iters) {
+    float mx = z;
+#pragma unroll
+    for (int s = 1; s < N; s <<= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, s, 64));
+    float m = expf(z - mx);
+    for (int it = 0; it < iters; ++it) {
+        float rs = m;
+#pragma unroll
+        for (int s = 1; s < N; s <<= 1)
+            rs += __shfl_xor(rs, s, 64);
+        m = m / rs;
+        float cs = m;
+#pragma unroll
+        for (int s = N; s < N * N; s <<= 1)
+            cs += __shfl_xor(cs, s, 64);
+        m = m / cs;
+    }
+    return m;
+}
+
+__device__ __forceinline__ float logistic(float v) { return 1.0f / (1.0f + expf(-v)); }
+
+}  // namespace ds4hc

@@ -1,0 +1,54 @@
+// hc_launch.hpp -- internal interface between the C ABI (ds4hc_api.cpp) and
+// the kernels (hc_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace ds4hc {
+
+// Arguments of one HC-pre / fused call after host-side validation.
+struct FusedArgs {
+    int n, d, dt, iters;
+    int64_t T;
+    float eps;
+    const void *X;
+    const uint16_t *W;
+    const float *bias;
+    const void *layer_out;  // fused only
+    void *layer_in;
+    float *coeffs;          // may be null
+    float *logits;          // may be null
+    void *X_out;            // fused only
+    float *ws;              // split-K workspace
+};
+
+int rowres_chunks(int d, int dt);
+int rowres_max_chunks(int n, int dt);
+int splitk_chunks(int n, int d, int dt);
+hipError_t launch_hc(const FusedArgs &a, bool fused, bool rowres, hipStream_t s);
+hipError_t launch_post(int n, int dt, int d, int64_t T, const void *X, const float *coeffs,
+                       const void *layer_out, void *X_out, hipStream_t s);
+hipError_t launch_sinkhorn(int n, int iters, int64_t T, const float *Z, float *H, hipStream_t s);
+
+// hipLaunchKernel with the kernel's own parameter types, so the launch status
+// comes back directly instead of through the thread's sticky last-error slot.
+template <typename... KArgs, std::size_t... I>
+hipError_t launch_tuple(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                        std::tuple<KArgs...> &tup, std::index_sequence<I...>) {
+    void *argv[sizeof...(KArgs) + 1] = {(void *)&std::get<I>(tup)..., nullptr};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), grid, block, argv, 0, s);
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                         Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> tup(static_cast<KArgs>(args)...);
+    return launch_tuple(kern, grid, block, s, tup, std::index_sequence_for<KArgs...>{});
+}
+
+}  // namespace ds4hc

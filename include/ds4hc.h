@@ -1,0 +1,164 @@
+/*
+ * ds4hc.h -- C ABI of libds4hc.so, the MI355X (gfx950) implementation of the
+ * DeepSeek-V4 hyper-connection (HC) op.
+ *
+ * The op, as the lucebox pages describe it:
+ *   - lucebox PR #496 "feat(ds4): add DSpark speculative runtime +
+ *     optimizations", PR body: a fused DS4 hyper-connection op
+ *     (GGML_OP_DS4_HC) with a register-resident Sinkhorn kernel.
+ *   - lucebox-hub PR #494 "fix(ds4): keep ROCmFPX generation byte-safe":
+ *     "HC-pre" as a decode cost centre (comment with the timing breakdown);
+ *     commit notes on the HC fn matvecs, hc_post and the GPU HC pre-mix;
+ *     the comment on the Sinkhorn kernel specialised for NHC = 4; and the
+ *     direct HC-pre API left out of that PR.
+ *   - lucebox PR #507 "correct layer-split HC handoff and per-device state",
+ *     Summary/Implementation: the full HC state flows between layers, the HC
+ *     fn weights are held as F16 per device, and HC scratch must be per
+ *     device (a shared scratch buffer was a bug there).
+ *
+ * Definitions (n = n_hc streams, d features, K = n*d, m = 2n + n*n):
+ *   X[t]      state of token t: n streams x d features, row-major
+ *             (flattened index k = i*d + c).
+ *   r         = sqrt(sum_k X[t]_k^2 / K + rms_eps)
+ *   z_j       = sum_k W[j][k] * X[t]_k / r + bias[j]             (fn matvec)
+ *   pre_i     = 1/(1+exp(-z_i)),  post_i = 1/(1+exp(-z_{n+i}))  (gates)
+ *   H         = Sinkhorn of Z[i][j] = z_{2n+i*n+j}: M = exp(Z - rowmax(Z)),
+ *               then sinkhorn_iters x (divide rows by their sums, then
+ *               columns by their sums).
+ *   layer_in[c] = sum_i pre_i * X[i][c]                           (pre-mix)
+ *   X'[i][c]    = sum_j H[i][j] * X[j][c] + post_i * layer_out[c]  (hc_post)
+ *   coeffs[t] = pre[0..n) | post[0..n) | H row-major [n*n]  (m floats)
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers on the calling thread's current
+ *     HIP device, 16-byte aligned, dense row-major with the shapes given.
+ *     The caller owns every buffer; the library allocates no device memory
+ *     and keeps no mutable global state, so it is re-entrant and thread-safe.
+ *   - Work is enqueued on `stream` (0 = the default stream) and the call
+ *     returns without waiting. Faults during execution surface at the
+ *     caller's next synchronisation of that stream.
+ *   - Arguments are validated on the host before any HIP call. A rejected
+ *     call enqueues nothing.
+ *   - State dtype (X, layer_in, layer_out, X_out): float32 or bfloat16.
+ *     Coefficients, logits and bias are float32; W is IEEE float16.
+ *     Arithmetic is float32 with one round-to-nearest-even at each store.
+ *   - Every path is deterministic: no floating-point atomics, fixed
+ *     reduction orders. Repeated calls on equal inputs give equal bits.
+ *   - T = 0 returns DS4HC_OK once the scalar arguments are valid, without
+ *     looking at any pointer (zero-size buffers may be NULL); nothing runs.
+ *   - Supported on the GPU: n_hc in {1, 2, 4}; d > 0 with d % 8 == 0;
+ *     0 <= T <= 2^24; sinkhorn_iters in [0, 1000].
+ */
+#ifndef DS4HC_H
+#define DS4HC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DS4HC_ABI_VERSION 1
+
+typedef enum {
+    DS4HC_OK = 0,
+    DS4HC_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad shape, small workspace, overlap */
+    DS4HC_ERR_UNSUPPORTED = 2, /* valid for the op, not supported by this GPU library */
+    DS4HC_ERR_HIP = 3          /* a HIP launch failed; see ds4hc_last_hip_error() */
+} ds4hc_status;
+
+typedef enum {
+    DS4HC_F32 = 0,  /* state stored as IEEE float32 */
+    DS4HC_BF16 = 1  /* state stored as bfloat16 (uint16 bit patterns) */
+} ds4hc_dtype;
+
+/* Operation constants. Defaults: rms_eps = 1e-6f, sinkhorn_iters = 20. */
+typedef struct {
+    int32_t n_hc;           /* streams n: 1, 2 or 4 on the GPU */
+    int32_t d;              /* features per stream, d % 8 == 0 */
+    float rms_eps;          /* added to the mean square inside the sqrt, >= 0 */
+    int32_t sinkhorn_iters; /* row-then-column normalisation rounds, 0..1000 */
+    uint32_t flags;         /* DS4HC_FLAG_* */
+} ds4hc_params;
+
+/* Every path is deterministic already; the flag is accepted and changes nothing. */
+#define DS4HC_FLAG_DETERMINISTIC 1u
+/* Force the token-parallel (one token per workgroup, row kept on chip) kernel,
+ * or the split-K kernels (partials over K chunks, then a combining kernel).
+ * Both compute the same op; the default picks by T. Forcing both is invalid. */
+#define DS4HC_FLAG_FORCE_ROWRES 2u
+#define DS4HC_FLAG_FORCE_SPLITK 4u
+
+/*
+ * ds4hc_pre -- HC-pre: RMS statistic, fn matvec, sigmoid gates, Sinkhorn and
+ * the pre-mix ("HC-pre" and the GPU "HC pre-mix", lucebox-hub PR #494).
+ *   X          [T, n, d]  state dtype       (read)
+ *   W_f16      [m, n*d]   float16 bits      (read)
+ *   bias       [m]        float32           (read)
+ *   layer_in   [T, d]     state dtype       (written)
+ *   coeffs     [T, m]     float32           (written: pre | post | H)
+ *   logits_opt [T, m]     float32 or NULL   (written: raw z, for debugging)
+ *   workspace  device scratch of at least ds4hc_workspace_bytes(p, T, dtype)
+ *              bytes (may be NULL when that is 0); contents need not be set
+ *              and are overwritten. Calls that share one workspace must be
+ *              ordered on one stream.
+ * Outputs must not overlap inputs or each other.
+ */
+ds4hc_status ds4hc_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                       const uint16_t *W_f16, const float *bias, void *layer_in, float *coeffs,
+                       float *logits_opt, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * ds4hc_sinkhorn -- the register-resident Sinkhorn micro-kernel alone (the
+ * NHC = 4 template kernel of lucebox-hub PR #494's comment on its 95 us ->
+ * 5.3 us fix), on arbitrary residual logits.
+ *   logits_res [T, n, n] float32 (read), H [T, n, n] float32 (written).
+ * n_hc in {1, 2, 4}; iters in [0, 1000]. H may not overlap logits_res.
+ */
+ds4hc_status ds4hc_sinkhorn(int64_t T, int32_t n_hc, int32_t iters, const float *logits_res,
+                            float *H, hipStream_t stream);
+
+/*
+ * ds4hc_post -- hc_post (lucebox-hub PR #494 commit notes): the post update
+ * X' = H.X + post (x) layer_out from coefficients written by ds4hc_pre.
+ *   X [T, n, d] state (read), coeffs [T, m] float32 (read),
+ *   layer_out [T, d] state (read), X_out [T, n, d] state (written).
+ * X_out may be exactly X (in-place update); any other overlap is invalid.
+ */
+ds4hc_status ds4hc_post(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                        const float *coeffs, const void *layer_out, void *X_out,
+                        hipStream_t stream);
+
+/*
+ * ds4hc_fused -- the whole op (GGML_OP_DS4_HC of lucebox PR #496) in one
+ * call, for a layer_out that does not depend on this call's layer_in.
+ * Arguments as in ds4hc_pre and ds4hc_post; coeffs_opt may be NULL.
+ * X_out may be exactly X; layer_in must not overlap X, X_out or layer_out.
+ */
+ds4hc_status ds4hc_fused(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                         const uint16_t *W_f16, const float *bias, const void *layer_out,
+                         void *layer_in, float *coeffs_opt, void *X_out, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes ds4hc_pre / ds4hc_fused need for these arguments (0 when
+ * the chosen path needs none). Pure function; 0 for invalid arguments. */
+size_t ds4hc_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype);
+
+/* Static, human-readable name of a status code. */
+const char *ds4hc_status_string(ds4hc_status s);
+
+/* Text of the last HIP error seen by a ds4hc call on this thread ("" if none). */
+const char *ds4hc_last_hip_error(void);
+
+/* DS4HC_ABI_VERSION of the loaded library. */
+int ds4hc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS4HC_H */

@@ -1,0 +1,195 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/*.h, and rejects bad arguments on the host before any
+HIP call (a rejected call enqueues nothing).
+
+The argument-validation tests pass fake (never dereferenced) device
+addresses, so they only run where no GPU is visible: there, even a
+validation bug could not launch a kernel on them.
+"""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from deepseek_v4_hyper_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation runs without a GPU")
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(ds4hc_\w+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused"):
+        assert want in names
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_status_strings():
+    assert B.abi_version() == 1
+    assert B.status_string(0) == "DS4HC_OK"
+    assert B.status_string(1) == "DS4HC_ERR_INVALID_ARG"
+    assert B.status_string(2) == "DS4HC_ERR_UNSUPPORTED"
+    assert B.status_string(3) == "DS4HC_ERR_HIP"
+    assert B.load().ds4hc_last_hip_error() == b""
+
+
+def test_workspace_bytes_is_pure_and_path_dependent():
+    p = B.make_params(4, 4096)
+    # decode-sized T takes the split-K path: chunks * T * (m + 1) floats
+    P = (4 * 4096) // 256
+    assert B.ds4hc_workspace_bytes(p, 1, B.DS4HC_F32) == P * 1 * 25 * 4
+    assert B.ds4hc_workspace_bytes(p, 4, B.DS4HC_F32) == P * 4 * 25 * 4
+    Pb = (4 * 4096) // 512
+    assert B.ds4hc_workspace_bytes(p, 4, B.DS4HC_BF16) == Pb * 4 * 25 * 4
+    # large T: the row-resident kernel needs no workspace
+    assert B.ds4hc_workspace_bytes(p, 4096, B.DS4HC_F32) == 0
+    pf = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_SPLITK)
+    assert B.ds4hc_workspace_bytes(pf, 4096, B.DS4HC_F32) == P * 4096 * 25 * 4
+    pr = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_ROWRES)
+    assert B.ds4hc_workspace_bytes(pr, 1, B.DS4HC_F32) == 0
+    # invalid arguments give 0
+    assert B.ds4hc_workspace_bytes(B.make_params(4, 4095), 1, B.DS4HC_F32) == 0
+    assert B.ds4hc_workspace_bytes(B.make_params(3, 4096), 1, B.DS4HC_F32) == 0
+
+
+# ------------------------------------------------------------------ validation
+
+A = 1 << 40  # fake, 16-byte-aligned device addresses, far apart
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(A * (i + 1) + off)
+
+
+def fused(p, T=8, dt=B.DS4HC_F32, **over):
+    args = dict(X=fake(0), W=fake(1), bias=fake(2), layer_out=fake(3), layer_in=fake(4),
+                coeffs=fake(5), X_out=fake(6), ws=fake(7), ws_bytes=1 << 30)
+    args.update(over)
+    return B.ds4hc_fused_raw(p, T, dt, args["X"], args["W"], args["bias"], args["layer_out"],
+                             args["layer_in"], args["coeffs"], args["X_out"], args["ws"],
+                             args["ws_bytes"], None)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("n,d,iters,eps,flags,dt,T,want", [
+    (4, 4096, 20, 1e-6, 0, 5, 8, B.DS4HC_ERR_INVALID_ARG),          # unknown dtype
+    (4, 4096, 20, 1e-6, 0, 0, -1, B.DS4HC_ERR_INVALID_ARG),         # T < 0
+    (0, 4096, 20, 1e-6, 0, 0, 8, B.DS4HC_ERR_INVALID_ARG),          # n < 1
+    (4, 0, 20, 1e-6, 0, 0, 8, B.DS4HC_ERR_INVALID_ARG),             # d <= 0
+    (4, 4100, 20, 1e-6, 0, 0, 8, B.DS4HC_ERR_INVALID_ARG),          # d % 8 != 0
+    (4, 4096, -1, 1e-6, 0, 0, 8, B.DS4HC_ERR_INVALID_ARG),          # iters < 0
+    (4, 4096, 20, -1.0, 0, 0, 8, B.DS4HC_ERR_INVALID_ARG),          # eps < 0
+    (4, 4096, 20, float("nan"), 0, 0, 8, B.DS4HC_ERR_INVALID_ARG),  # eps NaN
+    (4, 4096, 20, 1e-6, 64, 0, 8, B.DS4HC_ERR_INVALID_ARG),         # unknown flag
+    (4, 4096, 20, 1e-6, 6, 0, 8, B.DS4HC_ERR_INVALID_ARG),          # both force flags
+    (3, 4096, 20, 1e-6, 0, 0, 8, B.DS4HC_ERR_UNSUPPORTED),          # n = 3
+    (8, 4096, 20, 1e-6, 0, 0, 8, B.DS4HC_ERR_UNSUPPORTED),          # n = 8
+    (4, 4096, 1001, 1e-6, 0, 0, 8, B.DS4HC_ERR_UNSUPPORTED),        # iters too many
+    (4, 4096, 20, 1e-6, 0, 0, (1 << 24) + 1, B.DS4HC_ERR_UNSUPPORTED),  # T too large
+    (4, 65536, 20, 1e-6, 2, 0, 64, B.DS4HC_ERR_UNSUPPORTED),        # row too long to force rowres
+    (4, 4096, 20, 1e-6, 0, 0, 0, B.DS4HC_OK),                       # T = 0: nothing to do
+])
+def test_fused_rejects_bad_params(n, d, iters, eps, flags, dt, T, want):
+    p = B.make_params(n, d, eps, iters, flags)
+    assert fused(p, T, dt) == want
+
+
+@no_gpu_only
+@pytest.mark.parametrize("field", ["X", "W", "bias", "layer_out", "layer_in", "X_out"])
+def test_fused_rejects_null_pointers(field):
+    p = B.make_params(4, 4096)
+    assert fused(p, **{field: None}) == B.DS4HC_ERR_INVALID_ARG
+
+
+@no_gpu_only
+@pytest.mark.parametrize("field,off", [("X", 4), ("W", 8), ("layer_in", 2), ("layer_out", 12),
+                                       ("X_out", 4), ("bias", 2), ("coeffs", 1), ("ws", 2)])
+def test_fused_rejects_misaligned(field, off):
+    p = B.make_params(4, 4096)
+    idx = {"X": 0, "W": 1, "bias": 2, "layer_out": 3, "layer_in": 4, "coeffs": 5, "X_out": 6,
+           "ws": 7}[field]
+    assert fused(p, **{field: fake(idx, off)}) == B.DS4HC_ERR_INVALID_ARG
+
+
+@no_gpu_only
+def test_fused_rejects_small_workspace():
+    p = B.make_params(4, 4096)
+    need = B.ds4hc_workspace_bytes(p, 4, B.DS4HC_F32)
+    assert need > 0
+    assert fused(p, 4, ws_bytes=need - 4) == B.DS4HC_ERR_INVALID_ARG
+    assert fused(p, 4, ws=None) == B.DS4HC_ERR_INVALID_ARG
+
+
+@no_gpu_only
+def test_fused_rejects_overlaps_but_allows_in_place():
+    p = B.make_params(4, 4096)
+    T = 64  # row-resident path: no workspace
+    # layer_in inside X
+    assert fused(p, T, layer_in=fake(0, 4096)) == B.DS4HC_ERR_INVALID_ARG
+    # X_out overlapping X by a shifted window
+    assert fused(p, T, X_out=fake(0, 16)) == B.DS4HC_ERR_INVALID_ARG
+    # coeffs inside W
+    assert fused(p, T, coeffs=fake(1, 64)) == B.DS4HC_ERR_INVALID_ARG
+    # X_out exactly X is allowed: validation passes, so without a GPU the launch fails (ERR_HIP)
+    assert fused(p, T, X_out=fake(0)) == B.DS4HC_ERR_HIP
+    assert B.load().ds4hc_last_hip_error() != b""
+
+
+@no_gpu_only
+def test_pre_post_sinkhorn_validation():
+    p = B.make_params(4, 4096)
+    vp = fake
+    # pre requires coeffs
+    assert B.ds4hc_pre_raw(p, 8, 0, vp(0), vp(1), vp(2), vp(3), None, None, vp(7), 1 << 30,
+                           None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_pre_raw(p, 0, 0, vp(0), vp(1), vp(2), vp(3), vp(4), None, None, 0,
+                           None) == B.DS4HC_OK
+    # post: X_out may be X; partial overlap rejected; null rejected
+    assert B.ds4hc_post_raw(p, 8, 0, vp(0), vp(1), vp(2), vp(0, 16), None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_post_raw(p, 8, 0, vp(0), None, vp(2), vp(3), None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_post_raw(p, 0, 0, vp(0), vp(1), vp(2), vp(0), None) == B.DS4HC_OK
+    # sinkhorn
+    assert B.ds4hc_sinkhorn_raw(8, 3, 20, vp(0), vp(1), None) == B.DS4HC_ERR_UNSUPPORTED
+    assert B.ds4hc_sinkhorn_raw(8, 0, 20, vp(0), vp(1), None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_sinkhorn_raw(8, 4, -1, vp(0), vp(1), None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_sinkhorn_raw(8, 4, 20, vp(0), vp(0, 4), None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_sinkhorn_raw(0, 4, 20, vp(0), vp(1), None) == B.DS4HC_OK
+    # zero tokens: pointers are not looked at
+    assert B.ds4hc_sinkhorn_raw(0, 4, 20, None, None, None) == B.DS4HC_OK
+    assert B.ds4hc_post_raw(p, 0, 0, None, None, None, None, None) == B.DS4HC_OK
+    assert B.ds4hc_pre_raw(p, 0, 0, None, None, None, None, None, None, None, 0,
+                           None) == B.DS4HC_OK
+    assert fused(p, 0, X=None, W=None, layer_in=None, ws=None) == B.DS4HC_OK

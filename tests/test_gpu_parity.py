@@ -1,0 +1,298 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded inputs, for every workload and both kernel paths.
+
+Small and reduced-T cases are compared on every output element; the
+full-size prefill and stress workloads, in the launch configuration the
+benchmark times, are compared on sampled token rows the oracle computes one
+by one (rows are independent).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from deepseek_v4_hyper_amd import binding as B
+from deepseek_v4_hyper_amd import workloads as wl
+from hc_testlib import (TOL, assert_close_rows, assert_coeffs, case_to_device, say,
+                        state_to_torch, torch_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+FLAGS = {"default": 0, "rowres": B.DS4HC_FLAG_FORCE_ROWRES, "splitk": B.DS4HC_FLAG_FORCE_SPLITK}
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def run_fused(case, flags=0, X=None):
+    torch = torch_mod()
+    Xd, W, b, lo = case_to_device(case)
+    if X is not None:
+        Xd = X
+    say(f"[gpu] ds4hc_fused {case.name} T={case.T} n={case.n} d={case.d} {case.dtype} flags={flags}")
+    li, c, xo = B.ds4hc_fused(Xd, W, b, lo, rms_eps=case.eps, sinkhorn_iters=case.iters,
+                              flags=flags)
+    torch.cuda.synchronize()
+    return torch_to_f64(li), c.cpu().numpy().astype(np.float64), torch_to_f64(xo)
+
+
+def oracle_fused(case, rows=None):
+    X = wl.state_to_f64(case.X if rows is None else case.X[rows], case.dtype)
+    lo = wl.state_to_f64(case.layer_out if rows is None else case.layer_out[rows], case.dtype)
+    return oracle.fused(X, case.W, case.bias, lo, case.eps, case.iters)
+
+
+def check_full(case, got, what):
+    li, c, xo = got
+    rli, rc, rxo = oracle_fused(case)
+    tol = TOL[case.dtype]
+    e1 = assert_close_rows(li, rli, tol, f"{what} layer_in")
+    e2 = assert_close_rows(xo, rxo, tol, f"{what} X_out")
+    e3 = assert_coeffs(c, rc, f"{what} coeffs")
+    say(f"    errors: layer_in {e1:.2e}  X_out {e2:.2e}  coeffs {e3:.2e}")
+
+
+# ------------------------------------------------------------------ workloads, every element
+
+@pytest.mark.parametrize("path", ["default", "rowres", "splitk"])
+def test_single_token(path):
+    case = wl.make_single(0)
+    check_full(case, run_fused(case, FLAGS[path]), f"single/{path}")
+
+
+@pytest.mark.parametrize("path", ["default", "rowres", "splitk"])
+def test_verify_batch(path):
+    case = wl.make_verify(0)
+    check_full(case, run_fused(case, FLAGS[path]), f"verify/{path}")
+
+
+@pytest.mark.parametrize("path", ["default", "rowres", "splitk"])
+@pytest.mark.parametrize("T", [37, 67])
+def test_prefill_reduced_T(path, T):
+    """Prefill shape and value recipe (per-token log-uniform scales) at a T the
+    oracle finishes in seconds; 37 / 67 leave ragged tails on both paths."""
+    case = wl.make_prefill(1, T=T)
+    check_full(case, run_fused(case, FLAGS[path]), f"prefill T={T}/{path}")
+
+
+@pytest.mark.parametrize("path", ["default", "rowres", "splitk"])
+def test_stress_reduced_T(path):
+    """Stress recipe (bf16, residual logit std ~20, 5 % zero rows) at T = 41, d = 7168:
+    d is not a multiple of the row-resident chunk, so the last chunk is ragged."""
+    case = wl.make_stress(2, T=41)
+    assert len(case.zero_rows) == 2
+    got = run_fused(case, FLAGS[path])
+    check_full(case, got, f"stress T=41/{path}")
+    li = got[0]
+    assert np.all(li[case.zero_rows] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("n,d", [(1, 8), (1, 1032), (2, 264), (2, 4096), (4, 8), (4, 2056),
+                                 (4, 16384)])
+@pytest.mark.parametrize("path", ["rowres", "splitk"])
+def test_shapes(dtype, n, d, path):
+    cap = (7 if dtype == wl.F32 else 5) if n == 4 else 8
+    rowres_limit = cap * 256 * (4 if dtype == wl.F32 else 8)
+    if path == "rowres" and d > rowres_limit:
+        pytest.skip("row too long for the row-resident kernel")
+    case = wl.make_random(3 + n + d, 5, n, d, dtype)
+    check_full(case, run_fused(case, FLAGS[path]), f"n={n} d={d} {dtype}/{path}")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+
+def _sampled_check(case, flags, nsample, extra_rows=()):
+    torch = torch_mod()
+    got_li, got_c, got_xo = run_fused(case, flags)
+    rng = np.random.Generator(np.random.PCG64(123))
+    rows = np.unique(np.concatenate([[0, case.T - 1], rng.choice(case.T, nsample, replace=False),
+                                     np.asarray(extra_rows, dtype=np.int64)])).astype(np.int64)
+    rli, rc, rxo = oracle_fused(case, rows)
+    tol = TOL[case.dtype]
+    e1 = assert_close_rows(got_li[rows], rli, tol, f"{case.name} layer_in")
+    e2 = assert_close_rows(got_xo[rows], rxo, tol, f"{case.name} X_out")
+    e3 = assert_coeffs(got_c[rows], rc, f"{case.name} coeffs")
+    say(f"    {len(rows)} sampled rows: layer_in {e1:.2e}  X_out {e2:.2e}  coeffs {e3:.2e}")
+    # properties that hold for every row at any size
+    assert np.all(np.isfinite(got_xo)) and np.all(np.isfinite(got_li))
+    H = got_c[:, 2 * case.n:].reshape(case.T, case.n, case.n)
+    assert np.abs(H.sum(axis=1) - 1.0).max() < 1e-5      # columns normalised last
+    assert np.all((got_c >= 0) & (got_c <= 1))
+    del torch
+    return got_li, got_c, got_xo
+
+
+def test_prefill_full_size_sampled():
+    case = wl.make_prefill(0)
+    _sampled_check(case, 0, 96)
+
+
+def test_stress_full_size_sampled():
+    case = wl.make_stress(0)
+    li, c, xo = _sampled_check(case, 0, 64, extra_rows=case.zero_rows[:16])
+    # every all-zero row: layer_in = 0, pre = post = 1/2, H = 1/n, X' = layer_out / 2 (bf16-exact)
+    zr = case.zero_rows
+    assert np.all(li[zr] == 0.0)
+    assert np.all(c[zr, :8] == 0.5) and np.all(c[zr, 8:] == 0.25)
+    lo = wl.state_to_f64(case.layer_out[zr], case.dtype)
+    np.testing.assert_array_equal(xo[zr], np.repeat(0.5 * lo[:, None, :], case.n, axis=1))
+
+
+# ------------------------------------------------------------------ decode chain
+
+def test_decode_chain_43_layers():
+    """43 x (HC-pre -> stand-in layer body -> hc_post), stream-ordered, one sync.
+    Checked per layer under teacher forcing (oracle fed the GPU's X_l) and end to end."""
+    torch = torch_mod()
+    case = wl.make_chain(0)
+    n, d = case.n, case.d
+    X = state_to_torch(case.X, case.dtype)
+    b = torch.zeros(case.m, dtype=torch.float32, device="cuda")
+    Ws = [torch.from_numpy(w).cuda() for w in case.chain_W]
+    noise = torch.from_numpy(case.chain_noise).cuda()
+    states = [X.clone()]
+    ins, coeffs = [], []
+    say("[gpu] decode chain: 43 layers, T=1, d=4096")
+    for l in range(len(Ws)):
+        li, c, _ = B.ds4hc_pre(X, Ws[l], b)
+        lo = li * 0.5 + noise[l][None, :]
+        X = B.ds4hc_post(X, c, lo)
+        states.append(X)
+        ins.append(li)
+        coeffs.append(c)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for l in range(len(Ws)):
+        Xl = torch_to_f64(states[l])
+        rli, rc, _ = oracle.pre(Xl, case.chain_W[l], case.bias)
+        lo = torch_to_f64(ins[l]) * 0.5 + case.chain_noise[l].astype(np.float64)[None, :]
+        rx = oracle.post(Xl, rc, lo)
+        worst = max(worst, assert_close_rows(torch_to_f64(ins[l]), rli, TOL[wl.F32], f"layer {l} layer_in"),
+                    assert_close_rows(torch_to_f64(states[l + 1]), rx, TOL[wl.F32], f"layer {l} X'"))
+        assert_coeffs(coeffs[l].cpu().numpy(), rc, f"layer {l} coeffs")
+    ref = oracle.chain(wl.state_to_f64(case.X, case.dtype), case.chain_W, case.bias, case.chain_noise)
+    e2e = assert_close_rows(torch_to_f64(states[-1]), ref[-1], 1e-4, "chain end to end")
+    say(f"    teacher-forced worst {worst:.2e}; end-to-end {e2e:.2e}")
+
+
+# ------------------------------------------------------------------ Sinkhorn alone
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+@pytest.mark.parametrize("iters", [0, 1, 7, 20, 200])
+def test_sinkhorn_random(n, iters):
+    torch = torch_mod()
+    rng = np.random.Generator(np.random.PCG64(n * 1000 + iters))
+    Z = (rng.standard_normal((1000, n, n)) * 3).astype(np.float32)
+    say(f"[gpu] ds4hc_sinkhorn n={n} iters={iters}")
+    H = B.ds4hc_sinkhorn(torch.from_numpy(Z).cuda(), iters=iters).cpu().numpy()
+    assert_coeffs(H, oracle.sinkhorn(Z, iters), "sinkhorn")
+
+
+def test_sinkhorn_closed_forms():
+    torch = torch_mod()
+    P = np.zeros((4, 4))
+    P[np.arange(4), [1, 2, 3, 0]] = 1
+    Zs = np.stack([np.zeros((4, 4)), 5 * P, 90 * P, 200 * P]).astype(np.float32)
+    say("[gpu] ds4hc_sinkhorn closed forms")
+    H = B.ds4hc_sinkhorn(torch.from_numpy(Zs).cuda(), iters=20).cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(H[0], 0.25)
+    for k, c in ((1, 5.0), (2, 90.0)):
+        # closed form ((e^c - 1) P + J) / (e^c + n - 1); at c = 90 the off-diagonal
+        # 1/(e^90 + 3) = 8.2e-40 is a float32 subnormal, and exp(90) itself would
+        # overflow float32 without the max subtraction
+        want = (np.expm1(c) * P + 1) / (np.exp(c) + 3)
+        np.testing.assert_allclose(H[k], want, rtol=1e-5, atol=1e-44)
+    np.testing.assert_array_equal(H[3], P)   # e^-200 underflows to 0 in float32
+
+
+# ------------------------------------------------------------------ API behaviour on the GPU
+
+def test_pre_then_post_equals_fused_bitwise():
+    torch = torch_mod()
+    case = wl.make_prefill(4, T=64)
+    X, W, b, lo = case_to_device(case)
+    say("[gpu] pre+post vs fused, T=64")
+    li1, c1, xo1 = B.ds4hc_fused(X, W, b, lo)
+    li2, c2, _ = B.ds4hc_pre(X, W, b)
+    xo2 = B.ds4hc_post(X, c2, lo)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(li1, li2) and torch.equal(xo1, xo2)
+
+
+def test_in_place_update():
+    torch = torch_mod()
+    for T in (3, 50):
+        case = wl.make_prefill(5, T=T)
+        X, W, b, lo = case_to_device(case)
+        say(f"[gpu] in-place fused T={T}")
+        li_ref, c_ref, xo_ref = B.ds4hc_fused(X, W, b, lo)
+        Xi = X.clone()
+        li, c, xo = B.ds4hc_fused(Xi, W, b, lo, X_out=Xi)
+        torch.cuda.synchronize()
+        assert xo.data_ptr() == Xi.data_ptr()
+        assert torch.equal(Xi, xo_ref) and torch.equal(li, li_ref) and torch.equal(c, c_ref)
+
+
+def test_deterministic_repeats():
+    import hashlib
+    torch = torch_mod()
+    case = wl.make_prefill(6, T=512)
+    X, W, b, lo = case_to_device(case)
+    say("[gpu] 20 repeats, T=512 fused + T=4 fused")
+    small = wl.make_verify(6)
+    Xs, Ws, bs, los = case_to_device(small)
+    digests = set()
+    for _ in range(20):
+        outs = B.ds4hc_fused(X, W, b, lo) + B.ds4hc_fused(Xs, Ws, bs, los)
+        torch.cuda.synchronize()
+        h = hashlib.sha256()
+        for o in outs:
+            h.update(o.view(torch.uint8).cpu().numpy().tobytes())
+        digests.add(h.hexdigest())
+    assert len(digests) == 1
+
+
+def test_nan_row_stays_in_its_token():
+    torch = torch_mod()
+    case = wl.make_prefill(7, T=40)
+    X = case.X.copy()
+    X[11, 2, 100] = np.nan
+    say("[gpu] NaN propagation")
+    li, c, xo = run_fused(case, 0, X=state_to_torch(X, case.dtype))
+    assert np.all(np.isnan(li[11])) and np.all(np.isnan(xo[11])) and np.all(np.isnan(c[11]))
+    good = np.setdiff1d(np.arange(40), [11])
+    case.X = X
+    rli, rc, rxo = oracle_fused(case, good)
+    assert_close_rows(xo[good], rxo, TOL[wl.F32], "non-NaN rows")
+
+
+def test_zero_tokens_is_a_no_op():
+    torch = torch_mod()
+    X = torch.empty((0, 4, 256), device="cuda")
+    W = torch.zeros((24, 1024), dtype=torch.float16, device="cuda")
+    b = torch.zeros(24, device="cuda")
+    lo = torch.empty((0, 256), device="cuda")
+    li, c, xo = B.ds4hc_fused(X, W, b, lo)
+    torch.cuda.synchronize()
+    assert li.shape == (0, 256) and xo.shape == (0, 4, 256)
+
+
+@pytest.mark.parametrize("iters", [0, 1, 3])
+def test_iteration_counts(iters):
+    case = wl.make_prefill(8, T=40)
+    case.iters = iters
+    check_full(case, run_fused(case, 0), f"iters={iters}")
+
+
+def test_logits_output_matches_oracle():
+    torch = torch_mod()
+    case = wl.make_verify(9)
+    X, W, b, _ = case_to_device(case)
+    say("[gpu] ds4hc_pre logits")
+    for flags in (0, B.DS4HC_FLAG_FORCE_ROWRES):
+        li, c, z = B.ds4hc_pre(X, W, b, flags=flags, want_logits=True)
+        torch.cuda.synchronize()
+        _, _, rz = oracle.pre(wl.state_to_f64(case.X, case.dtype), case.W, case.bias)
+        assert_close_rows(z.cpu().numpy(), rz, 2e-5, "logits")
