@@ -31,6 +31,8 @@ HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ["deepseek_v4_hyper_amd/csrc/hc_kernels.hip",
                   "deepseek_v4_hyper_amd/csrc/hc_device.hpp",
                   "deepseek_v4_hyper_amd/csrc/hc_launch.hpp"]
+KERNEL_NAME = {"default": "hc_rowres_kernel", "tile": "hc_tile_kernel", "rowres": "hc_rowres_kernel",
+               "splitk": "hc_partials_kernel+hc_finish_kernel"}
 COUNTERS_FILE = {"prefill": "profiles/hc_rowres_prefill_T4096_counters.json",
                  "stress": "profiles/hc_rowres_stress_T16384_counters.json"}
 
@@ -135,6 +137,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill", choices=["prefill", "stress"])
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated across steps")
+    ap.add_argument("--path", default="default", choices=["default", "rowres", "tile", "splitk"],
+                    help="force one kernel path (default: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for counter scaling)")
@@ -162,7 +166,9 @@ def main():
         xo = torch.empty_like(X)
         sets.append((X, W, b, lo, li, cf, xo))
     dt = B.DS4HC_F32 if c0.dtype == wl.F32 else B.DS4HC_BF16
-    params = B.make_params(n, d, c0.eps, c0.iters, 0)
+    flags = {"default": 0, "rowres": B.DS4HC_FLAG_FORCE_ROWRES, "tile": B.DS4HC_FLAG_FORCE_TILE,
+             "splitk": B.DS4HC_FLAG_FORCE_SPLITK}[args.path]
+    params = B.make_params(n, d, c0.eps, c0.iters, flags)
     ws_bytes = B.ds4hc_workspace_bytes(params, T, dt)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -195,7 +201,8 @@ def main():
     sb = 4 if c0.dtype == wl.F32 else 2
     alg = algorithmic_bytes(T, n, d, sb)
     achieved = alg / (ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, kernel_source_hash())
+    traffic = load_traffic(args.workload, kernel_source_hash()) if args.path in ("default", "rowres") \
+        else None
     rec = {
         "metric": METRIC if args.workload == "prefill" else
         f"HC-op tokens/s and achieved HBM GB/s at T={T}, d={d}, n_hc={n} ({c0.dtype} state)",
@@ -212,12 +219,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: T={T}, n_hc={n}, d={d}, {c0.dtype} state, "
                                f"f16 fn weight [{m},{n * d}], {c0.iters} Sinkhorn iterations",
-                   "entry_point": "ds4hc_fused", "input_sets_rotated": len(sets),
+                   "entry_point": "ds4hc_fused", "path": args.path, "input_sets_rotated": len(sets),
                    "host_wall_s": round(wall, 4)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg,
-                     "kernel": "hc_rowres_kernel" if ws_bytes == 0 else "hc_partials+hc_finish"},
+                     "kernel": KERNEL_NAME[args.path]},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(c0)

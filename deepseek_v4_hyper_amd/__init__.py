@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     DS4HC_FLAG_DETERMINISTIC,
     DS4HC_FLAG_FORCE_ROWRES,
     DS4HC_FLAG_FORCE_SPLITK,
+    DS4HC_FLAG_FORCE_TILE,
     Ds4hcError,
     ds4hc_fused,
     ds4hc_post,

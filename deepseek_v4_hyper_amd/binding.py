@@ -23,6 +23,7 @@ DS4HC_BF16 = 1
 DS4HC_FLAG_DETERMINISTIC = 1
 DS4HC_FLAG_FORCE_ROWRES = 2
 DS4HC_FLAG_FORCE_SPLITK = 4
+DS4HC_FLAG_FORCE_TILE = 8
 
 EXPORTED = ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused", "ds4hc_workspace_bytes",
             "ds4hc_status_string", "ds4hc_last_hip_error", "ds4hc_abi_version")

@@ -21,8 +21,9 @@ constexpr int64_t SPLITK_MAX_T = 32;       // T at or below which split-K is the
 constexpr int64_t MAX_T = int64_t(1) << 24;
 constexpr int MAX_ITERS = 1000;
 constexpr uint64_t MAX_WORK_ITEMS = 0xFFFFFFFFull;  // HSA dispatch grid size is 32-bit
-constexpr uint32_t KNOWN_FLAGS =
-    DS4HC_FLAG_DETERMINISTIC | DS4HC_FLAG_FORCE_ROWRES | DS4HC_FLAG_FORCE_SPLITK;
+constexpr uint32_t FORCE_FLAGS =
+    DS4HC_FLAG_FORCE_ROWRES | DS4HC_FLAG_FORCE_TILE | DS4HC_FLAG_FORCE_SPLITK;
+constexpr uint32_t KNOWN_FLAGS = DS4HC_FLAG_DETERMINISTIC | FORCE_FLAGS;
 
 thread_local char g_last_hip_error[256] = "";
 
@@ -56,36 +57,49 @@ ds4hc_status check_params(const ds4hc_params *p, int64_t T, ds4hc_dtype dt) {
     if (!(p->rms_eps >= 0.f) || !isfinite(p->rms_eps)) return DS4HC_ERR_INVALID_ARG;
     if (p->sinkhorn_iters < 0) return DS4HC_ERR_INVALID_ARG;
     if (p->flags & ~KNOWN_FLAGS) return DS4HC_ERR_INVALID_ARG;
-    if ((p->flags & DS4HC_FLAG_FORCE_ROWRES) && (p->flags & DS4HC_FLAG_FORCE_SPLITK))
-        return DS4HC_ERR_INVALID_ARG;
+    const uint32_t force = p->flags & FORCE_FLAGS;
+    if (force & (force - 1)) return DS4HC_ERR_INVALID_ARG;  // more than one path forced
     if (p->n_hc != 1 && p->n_hc != 2 && p->n_hc != 4) return DS4HC_ERR_UNSUPPORTED;
     if (p->sinkhorn_iters > MAX_ITERS || T > MAX_T) return DS4HC_ERR_UNSUPPORTED;
     return DS4HC_OK;
 }
 
 struct Plan {
-    bool rowres;
+    int path;              // ds4hc::PATH_*
     int P;                 // split-K chunks
     uint64_t ws_bytes;     // workspace needed
 };
 
-// Path for HC-pre / fused. Returns UNSUPPORTED if a launch would not fit.
+// Path for HC-pre / fused: split-K for small T (the fn weight dominates the
+// bytes and must be spread over many CUs), the one-token VALU kernel for
+// large T (measured faster than the two-token MFMA tile kernel on MI355X at
+// T = 4096 and 16384), split-K where a row is too long for it.
+// Returns UNSUPPORTED if a forced path cannot take the shape or a launch
+// would not fit.
 ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *out) {
     const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
-    const int cq = ds4hc::rowres_chunks(d, dt);
-    const bool fits_rowres = cq <= ds4hc::rowres_max_chunks(n, dt);
-    bool rowres;
-    if (p->flags & DS4HC_FLAG_FORCE_ROWRES) {
+    const bool fits_rowres = ds4hc::rowres_chunks(d, dt) <= ds4hc::rowres_max_chunks(n, dt);
+    const bool fits_tile = ds4hc::tile_steps(d, dt) <= ds4hc::tile_max_steps();
+    const uint32_t force = p->flags & FORCE_FLAGS;
+    int path;
+    if (force == DS4HC_FLAG_FORCE_ROWRES) {
         if (!fits_rowres) return DS4HC_ERR_UNSUPPORTED;
-        rowres = true;
-    } else if (p->flags & DS4HC_FLAG_FORCE_SPLITK) {
-        rowres = false;
+        path = ds4hc::PATH_ROWRES;
+    } else if (force == DS4HC_FLAG_FORCE_TILE) {
+        if (!fits_tile) return DS4HC_ERR_UNSUPPORTED;
+        path = ds4hc::PATH_TILE;
+    } else if (force == DS4HC_FLAG_FORCE_SPLITK) {
+        path = ds4hc::PATH_SPLITK;
+    } else if (T <= SPLITK_MAX_T) {
+        path = ds4hc::PATH_SPLITK;
     } else {
-        rowres = fits_rowres && T > SPLITK_MAX_T;
+        path = fits_rowres ? ds4hc::PATH_ROWRES : fits_tile ? ds4hc::PATH_TILE : ds4hc::PATH_SPLITK;
     }
-    Plan pl{rowres, 0, 0};
-    if (rowres) {
+    Plan pl{path, 0, 0};
+    if (path == ds4hc::PATH_ROWRES) {
         if ((uint64_t)T * 256u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
+    } else if (path == ds4hc::PATH_TILE) {
+        if ((uint64_t)(T + 1) / 2 * 256u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
     } else {
         pl.P = ds4hc::splitk_chunks(n, d, dt);
         const uint64_t tg = (uint64_t)(T + 3) / 4;
@@ -141,7 +155,7 @@ ds4hc_status run_hc(bool fused, const ds4hc_params *p, int64_t T, ds4hc_dtype dt
 
     ds4hc::FusedArgs a{n, d, (int)dt, p->sinkhorn_iters, T, p->rms_eps, X, W, bias, layer_out,
                        layer_in, coeffs, logits, X_out, static_cast<float *>(workspace)};
-    const hipError_t e = ds4hc::launch_hc(a, fused, pl.rowres, stream);
+    const hipError_t e = ds4hc::launch_hc(a, fused, pl.path, stream);
     return e == hipSuccess ? DS4HC_OK : hip_fail(e);
 }
 

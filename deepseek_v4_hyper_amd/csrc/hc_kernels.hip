@@ -194,6 +194,312 @@ __global__ __launch_bounds__(ROWRES_THREADS) void hc_rowres_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// MFMA tile kernel: two tokens per 256-thread workgroup, rows kept in
+// registers, the fn matvec on v_mfma_f32_4x4x4_16b_f16.
+//
+// The fn projection z = W . x~ (x~ = x / r) is a [24 x K] . [K x 2] product
+// per workgroup. One 4x4x4_16b instruction is 16 independent 4x4x4 products
+// (block b = lane / 4): A_b = 4 rows of W x 4 consecutive k, B_b = 4 k x 4
+// columns, where the columns are (token 0 hi, token 0 lo, token 1 hi,
+// token 1 lo). x~ is split exactly into f16 hi + lo (hi = f16(x~),
+// lo = f16(x~ - hi)), so hi + lo carries x~ to ~2^-23 relative and the
+// products are exact; accumulation is fp32. |x~| <= sqrt(K), so f16 cannot
+// overflow. Lane 4b + 2t + p holds V state elements of token t (p = 0 the
+// first, p = 1 the second V of block b's 2V columns); a quad DPP swap hands
+// each lane the hi or lo half its column needs from its partner.
+//
+// Column step j of wave w covers STEP = 32*V columns of every stream:
+// columns (w + 4j)*STEP + b*2V + p*V .. +V-1, so every lane holds all n
+// streams of its columns and the post update needs no data exchange.
+// ---------------------------------------------------------------------------
+// Opaque register barrier: the compiler must assume the packed vector changed,
+// so it re-derives float32 values from it instead of keeping unpacked copies of
+// a whole register-resident row live across phases (which spills to scratch).
+template <int DT>
+__device__ __forceinline__ void launder(StateVec<DT> &v) {
+    asm volatile("" : "+v"(v.raw.x), "+v"(v.raw.y), "+v"(v.raw.z), "+v"(v.raw.w));
+}
+
+// Word 3 of a gfx9-family buffer resource descriptor (32-bit data format,
+// raw addressing); loads at or past num_records return zero.
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int uint2_t __attribute__((ext_vector_type(2)));
+
+constexpr int TILE_TOKENS = 2;
+constexpr int TILE_THREADS = 256;
+constexpr int TILE_WAVES = TILE_THREADS / 64;
+
+// Opaque register barrier on a 4 x f16 value: later uses see these exact bits.
+__device__ __forceinline__ void pin_half4(half4_t &v) {
+    uint2_t u = __builtin_bit_cast(uint2_t, v);
+    asm volatile("" : "+v"(u.x), "+v"(u.y));
+    v = __builtin_bit_cast(half4_t, u);
+}
+
+// Exchange a 4 x f16 value with the partner lane (lane ^ 1) of the quad.
+__device__ __forceinline__ half4_t quad_swap(half4_t v) {
+    uint2_t u = __builtin_bit_cast(uint2_t, v);
+    u.x = (unsigned)__builtin_amdgcn_mov_dpp((int)u.x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    u.y = (unsigned)__builtin_amdgcn_mov_dpp((int)u.y, 0xB1, 0xF, 0xF, false);
+    return __builtin_bit_cast(half4_t, u);
+}
+
+// Sub-block sb (4 consecutive float16) of a packed W slice, as an MFMA operand.
+template <int V>
+__device__ __forceinline__ half4_t half_sub4(const HalfVec<V> &h, int sb) {
+    uint2_t u;
+    if constexpr (V == 4) {
+        u.x = h.raw.x;
+        u.y = h.raw.y;
+    } else {
+        u.x = sb == 0 ? h.raw.x : h.raw.z;
+        u.y = sb == 0 ? h.raw.y : h.raw.w;
+    }
+    return __builtin_bit_cast(half4_t, u);
+}
+
+template <int N, int DT, int CS, int MODE>
+__global__ __launch_bounds__(TILE_THREADS, 2) void hc_tile_kernel(
+    int d, int T, float eps, int iters, const void *__restrict__ X, const uint16_t *__restrict__ W,
+    const float *__restrict__ bias, const void *__restrict__ layer_out, void *__restrict__ layer_in,
+    float *__restrict__ coeffs, float *__restrict__ logits, void *X_out) {
+    constexpr int V = StateVec<DT>::V;
+    constexpr int M = n_logits(N);
+    constexpr int G = (M + 3) / 4;  // groups of 4 W rows
+    constexpr int SB = V / 4;       // 4-element sub-blocks per lane vector
+    constexpr int STEP = 32 * V;    // columns per step
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // readfirstlane makes the wave index (and every offset built from it) a
+    // scalar the compiler can put in the buffer loads' scalar offset field.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int blk = lane >> 2;
+    const int t = (lane >> 1) & 1;
+    const int p = lane & 1;
+    const int row4 = lane & 3;
+    const size_t tok = (size_t)blockIdx.x * TILE_TOKENS + t;
+    const bool tok_ok = tok < (size_t)T;
+    const size_t K = (size_t)N * d;
+
+    __shared__ float ssr[TILE_WAVES][TILE_TOKENS];
+    __shared__ float zred[TILE_WAVES][4][G * 4];
+    __shared__ float zs[TILE_TOKENS][M];
+    __shared__ float cf[TILE_TOKENS][M];
+
+    // ---- phase 1: the two rows into registers, sum of squares ----
+    StateVec<DT> xv[N][CS];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < CS; ++j) {
+        const int c0 = (wave + TILE_WAVES * j) * STEP + blk * 2 * V + p * V;
+        const bool ok = tok_ok && c0 < d;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            xv[i][j] = ok ? load_vec<DT>(X, tok * K + (size_t)i * d + c0) : zero_vec<DT>();
+    }
+#pragma unroll
+    for (int j = 0; j < CS; ++j)
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float x = vec_get<DT>(xv[i][j], e);
+                ss = fmaf(x, x, ss);
+            }
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    ss += __shfl_xor(ss, 8, 64);
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (lane == 0 || lane == 2) ssr[wave][t] = ss;
+    __syncthreads();
+    float sst = ssr[0][t];
+#pragma unroll
+    for (int w = 1; w < TILE_WAVES; ++w) sst += ssr[w][t];
+    const float inv_r = 1.0f / sqrtf(sst / (float)K + eps);
+
+    // ---- phase 2: fn matvec on MFMA ----
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(W), (short)0, (int)((size_t)M * K * 2), BUFFER_RSRC_WORD3);
+    // W row 4g + row4 of every group through one descriptor: a per-lane byte
+    // offset plus a wave-uniform offset per (group, stream, step). Padding rows
+    // (>= M, when M % 4 != 0) fall past the end of W and read as zero.
+    const int w_voff = (int)((row4 * K + blk * 2 * V) * 2);
+#pragma unroll
+    for (int j = 0; j < CS; ++j)
+#pragma unroll
+        for (int i = 0; i < N; ++i) launder<DT>(xv[i][j]);
+    float4_t acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < CS; ++j) {
+        const int cs = wave + TILE_WAVES * j;
+        if (cs * STEP >= d) break;  // wave-uniform
+        const int cb = cs * STEP + blk * 2 * V;  // first column of block b
+        const bool e_ok = cb < d, o_ok = cb + V < d;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            // A operands: W rows 4g + row4, columns cb .. cb + 2V - 1 of stream i
+            HalfVec<V> we[G], wo[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int soff = (int)((4 * g * K + (size_t)i * d + (size_t)cs * STEP) * 2);
+                if constexpr (V == 4) {
+                    uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, soff, 0));
+                    if (!e_ok) u = make_uint4(0u, 0u, 0u, 0u);
+                    we[g].raw = make_uint2(u.x, u.y);
+                    wo[g].raw = make_uint2(u.z, u.w);
+                } else {
+                    uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, soff, 0));
+                    uint4 b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff + 16, soff, 0));
+                    if (!e_ok) a = make_uint4(0u, 0u, 0u, 0u);
+                    if (!o_ok) b = make_uint4(0u, 0u, 0u, 0u);
+                    we[g].raw = a;
+                    wo[g].raw = b;
+                }
+            }
+            half4_t hi[SB], lo[SB], rcv[SB];
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb) {
+                float xt[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xt[e] = vec_get<DT>(xv[i][j], 4 * sb + e) * inv_r;
+                    hi[sb][e] = (_Float16)xt[e];
+                }
+                // lo must be formed from the very bits the MFMA consumes as hi:
+                // left free, the compiler rounds x~ to f16 twice with two
+                // instructions that break ties differently, and hi + lo misses
+                // x~ by one f16 ulp on exact ties.
+                pin_half4(hi[sb]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lo[sb][e] = (_Float16)(xt[e] - (float)hi[sb][e]);
+                rcv[sb] = quad_swap(p ? hi[sb] : lo[sb]);
+            }
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb) {
+                const half4_t be = p ? rcv[sb] : hi[sb];  // block columns cb + 4sb ..
+                const half4_t bo = p ? lo[sb] : rcv[sb];  // block columns cb + V + 4sb ..
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(half_sub4<V>(we[g], sb), be,
+                                                                acc[g], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(half_sub4<V>(wo[g], sb), bo,
+                                                                acc[g], 0, 0, 0);
+            }
+        }
+    }
+
+    // layer_out for the post update: issued now, consumed after the reductions
+    // and the Sinkhorn, whose latency it hides.
+    StateVec<DT> lov[CS];
+    if constexpr (MODE == MODE_FUSED) {
+#pragma unroll
+        for (int j = 0; j < CS; ++j) {
+            const int c0 = (wave + TILE_WAVES * j) * STEP + blk * 2 * V + p * V;
+            lov[j] = (tok_ok && c0 < d) ? load_vec<DT>(layer_out, tok * d + c0) : zero_vec<DT>();
+        }
+    }
+
+    // ---- phase 3: sum the 16 blocks, then the waves, in a fixed order ----
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = acc[g][r];
+            v += __shfl_xor(v, 4, 64);
+            v += __shfl_xor(v, 8, 64);
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if (lane < 4) zred[wave][lane][4 * g + r] = v;
+        }
+    __syncthreads();
+    if (tid < TILE_TOKENS * M) {
+        const int tt = tid / M, row = tid % M;
+        float s = zred[0][2 * tt][row] + zred[0][2 * tt + 1][row];
+#pragma unroll
+        for (int w = 1; w < TILE_WAVES; ++w) s += zred[w][2 * tt][row] + zred[w][2 * tt + 1][row];
+        const float z = s + bias[row];
+        zs[tt][row] = z;
+        const size_t tk = (size_t)blockIdx.x * TILE_TOKENS + tt;
+        if (logits && tk < (size_t)T) logits[tk * M + row] = z;
+    }
+    __syncthreads();
+
+    // ---- phase 4: gates and Sinkhorn for both tokens (wave 0) ----
+    if (wave == 0) {
+        constexpr int NN = N * N;
+        const int grp = lane / NN, e = lane % NN, tt = grp & 1;
+        const float h = sinkhorn_lane<N>(zs[tt][2 * N + e], iters);
+        const size_t tk = (size_t)blockIdx.x * TILE_TOKENS + tt;
+        if (grp < TILE_TOKENS) {
+            cf[tt][2 * N + e] = h;
+            if (coeffs && tk < (size_t)T) coeffs[tk * M + 2 * N + e] = h;
+        }
+        if (lane < TILE_TOKENS * 2 * N) {
+            const int gt = lane / (2 * N), idx = lane % (2 * N);
+            const float gv = logistic(zs[gt][idx]);
+            cf[gt][idx] = gv;
+            const size_t gk = (size_t)blockIdx.x * TILE_TOKENS + gt;
+            if (coeffs && gk < (size_t)T) coeffs[gk * M + idx] = gv;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 5: pre-mix and post update from the registers ----
+#pragma unroll
+    for (int j = 0; j < CS; ++j)
+#pragma unroll
+        for (int i = 0; i < N; ++i) launder<DT>(xv[i][j]);
+    float pre[N], post[N], H[N][N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        pre[i] = cf[t][i];
+        post[i] = cf[t][N + i];
+#pragma unroll
+        for (int j = 0; j < N; ++j) H[i][j] = cf[t][2 * N + i * N + j];
+    }
+#pragma unroll
+    for (int j = 0; j < CS; ++j) {
+        const int c0 = (wave + TILE_WAVES * j) * STEP + blk * 2 * V + p * V;
+        if (!tok_ok || c0 >= d) continue;
+        float x[N][V];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+#pragma unroll
+            for (int e = 0; e < V; ++e) x[i][e] = vec_get<DT>(xv[i][j], e);
+        float li[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            float s = pre[0] * x[0][e];
+#pragma unroll
+            for (int i = 1; i < N; ++i) s = fmaf(pre[i], x[i][e], s);
+            li[e] = s;
+        }
+        store_vec<DT>(layer_in, tok * d + c0, li);
+        if constexpr (MODE == MODE_FUSED) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    float s = H[i][0] * x[0][e];
+#pragma unroll
+                    for (int jj = 1; jj < N; ++jj) s = fmaf(H[i][jj], x[jj][e], s);
+                    o[e] = fmaf(post[i], vec_get<DT>(lov[j], e), s);
+                }
+                store_vec<DT>(X_out, tok * K + (size_t)i * d + c0, o);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Split-K partials: grid (ceil(T / SPLITK_TOKENS), P chunks), one wavefront.
 // Chunk p covers flattened columns [p*64*V, (p+1)*64*V) of K; lane l owns V
 // consecutive columns. Writes ws[p][t][0..M) = partial dots, ws[p][t][M] =
@@ -411,6 +717,29 @@ static hipError_t launch_rowres_n(int cq, const FusedArgs &a, hipStream_t s) {
 }
 
 template <int N, int DT, int MODE>
+static hipError_t launch_tile_n(int cs, const FusedArgs &a, hipStream_t s) {
+    const dim3 grid((unsigned)((a.T + TILE_TOKENS - 1) / TILE_TOKENS)), block(TILE_THREADS);
+#define DS4HC_TILE_CASE(CS)                                                                      \
+    case CS:                                                                                     \
+        return launch_kernel(hc_tile_kernel<N, DT, CS, MODE>, grid, block, s, a.d, (int)a.T,     \
+                             a.eps, a.iters, a.X, a.W, a.bias, a.layer_out, a.layer_in,          \
+                             a.coeffs, a.logits, a.X_out);
+    switch (cs) {
+        DS4HC_TILE_CASE(1)
+        DS4HC_TILE_CASE(2)
+        DS4HC_TILE_CASE(3)
+        DS4HC_TILE_CASE(4)
+        DS4HC_TILE_CASE(5)
+        DS4HC_TILE_CASE(6)
+        DS4HC_TILE_CASE(7)
+        DS4HC_TILE_CASE(8)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef DS4HC_TILE_CASE
+}
+
+template <int N, int DT, int MODE>
 static hipError_t launch_splitk_n(const FusedArgs &a, hipStream_t s) {
     constexpr int V = StateVec<DT>::V;
     const int P = splitk_chunks(N, a.d, DT);
@@ -424,21 +753,23 @@ static hipError_t launch_splitk_n(const FusedArgs &a, hipStream_t s) {
                          a.coeffs, a.logits, a.X_out);
 }
 
-template <int N>
-static hipError_t dispatch_dt(int dt, bool fused, bool rowres, int cq, const FusedArgs &a,
-                              hipStream_t s) {
-    if (dt == DT_F32) {
-        if (rowres)
-            return fused ? launch_rowres_n<N, DT_F32, MODE_FUSED>(cq, a, s)
-                         : launch_rowres_n<N, DT_F32, MODE_PRE>(cq, a, s);
-        return fused ? launch_splitk_n<N, DT_F32, MODE_FUSED>(a, s)
-                     : launch_splitk_n<N, DT_F32, MODE_PRE>(a, s);
+template <int N, int DT, int MODE>
+static hipError_t dispatch_path(int path, const FusedArgs &a, hipStream_t s) {
+    switch (path) {
+    case PATH_ROWRES: return launch_rowres_n<N, DT, MODE>(rowres_chunks(a.d, DT), a, s);
+    case PATH_TILE: return launch_tile_n<N, DT, MODE>(tile_steps(a.d, DT), a, s);
+    case PATH_SPLITK: return launch_splitk_n<N, DT, MODE>(a, s);
     }
-    if (rowres)
-        return fused ? launch_rowres_n<N, DT_BF16, MODE_FUSED>(cq, a, s)
-                     : launch_rowres_n<N, DT_BF16, MODE_PRE>(cq, a, s);
-    return fused ? launch_splitk_n<N, DT_BF16, MODE_FUSED>(a, s)
-                 : launch_splitk_n<N, DT_BF16, MODE_PRE>(a, s);
+    return hipErrorInvalidValue;
+}
+
+template <int N>
+static hipError_t dispatch_dt(int dt, bool fused, int path, const FusedArgs &a, hipStream_t s) {
+    if (dt == DT_F32)
+        return fused ? dispatch_path<N, DT_F32, MODE_FUSED>(path, a, s)
+                     : dispatch_path<N, DT_F32, MODE_PRE>(path, a, s);
+    return fused ? dispatch_path<N, DT_BF16, MODE_FUSED>(path, a, s)
+                 : dispatch_path<N, DT_BF16, MODE_PRE>(path, a, s);
 }
 
 int rowres_chunks(int d, int dt) {
@@ -448,18 +779,25 @@ int rowres_chunks(int d, int dt) {
 
 int rowres_max_chunks(int n, int dt) { return rowres_cap(n, dt); }
 
+int tile_steps(int d, int dt) {
+    const int V = dt == DT_F32 ? 4 : 8;
+    const int steps = (d + 32 * V - 1) / (32 * V);
+    return (steps + TILE_WAVES - 1) / TILE_WAVES;
+}
+
+int tile_max_steps() { return 8; }
+
 int splitk_chunks(int n, int d, int dt) {
     const int V = dt == DT_F32 ? 4 : 8;
     const long K = (long)n * d;
     return (int)((K + 64 * V - 1) / (64 * V));
 }
 
-hipError_t launch_hc(const FusedArgs &a, bool fused, bool rowres, hipStream_t s) {
-    const int cq = rowres_chunks(a.d, a.dt);
+hipError_t launch_hc(const FusedArgs &a, bool fused, int path, hipStream_t s) {
     switch (a.n) {
-    case 1: return dispatch_dt<1>(a.dt, fused, rowres, cq, a, s);
-    case 2: return dispatch_dt<2>(a.dt, fused, rowres, cq, a, s);
-    case 4: return dispatch_dt<4>(a.dt, fused, rowres, cq, a, s);
+    case 1: return dispatch_dt<1>(a.dt, fused, path, a, s);
+    case 2: return dispatch_dt<2>(a.dt, fused, path, a, s);
+    case 4: return dispatch_dt<4>(a.dt, fused, path, a, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -26,10 +26,15 @@ struct FusedArgs {
     float *ws;              // split-K workspace
 };
 
+// Kernel paths for HC-pre / fused.
+enum : int { PATH_ROWRES = 0, PATH_TILE = 1, PATH_SPLITK = 2 };
+
 int rowres_chunks(int d, int dt);
 int rowres_max_chunks(int n, int dt);
+int tile_steps(int d, int dt);
+int tile_max_steps();
 int splitk_chunks(int n, int d, int dt);
-hipError_t launch_hc(const FusedArgs &a, bool fused, bool rowres, hipStream_t s);
+hipError_t launch_hc(const FusedArgs &a, bool fused, int path, hipStream_t s);
 hipError_t launch_post(int n, int dt, int d, int64_t T, const void *X, const float *coeffs,
                        const void *layer_out, void *X_out, hipStream_t s);
 hipError_t launch_sinkhorn(int n, int iters, int64_t T, const float *Z, float *H, hipStream_t s);

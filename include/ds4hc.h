@@ -86,11 +86,14 @@ typedef struct {
 
 /* Every path is deterministic already; the flag is accepted and changes nothing. */
 #define DS4HC_FLAG_DETERMINISTIC 1u
-/* Force the token-parallel (one token per workgroup, row kept on chip) kernel,
- * or the split-K kernels (partials over K chunks, then a combining kernel).
- * Both compute the same op; the default picks by T. Forcing both is invalid. */
+/* Force one kernel path (all compute the same op; the default picks by T and
+ * row length; forcing more than one is invalid):
+ *   ROWRES  one token per workgroup, row kept in registers, VALU matvec;
+ *   TILE    two tokens per workgroup, rows kept in registers, MFMA matvec;
+ *   SPLITK  partials over K chunks into the workspace, then a combining kernel. */
 #define DS4HC_FLAG_FORCE_ROWRES 2u
 #define DS4HC_FLAG_FORCE_SPLITK 4u
+#define DS4HC_FLAG_FORCE_TILE 8u
 
 /*
  * ds4hc_pre -- HC-pre: RMS statistic, fn matvec, sigmoid gates, Sinkhorn and

@@ -113,8 +113,10 @@ def fused(p, T=8, dt=B.DS4HC_F32, **over):
     (4, 4096, -1, 1e-6, 0, 0, 8, B.DS4HC_ERR_INVALID_ARG),          # iters < 0
     (4, 4096, 20, -1.0, 0, 0, 8, B.DS4HC_ERR_INVALID_ARG),          # eps < 0
     (4, 4096, 20, float("nan"), 0, 0, 8, B.DS4HC_ERR_INVALID_ARG),  # eps NaN
-    (4, 4096, 20, 1e-6, 64, 0, 8, B.DS4HC_ERR_INVALID_ARG),         # unknown flag
-    (4, 4096, 20, 1e-6, 6, 0, 8, B.DS4HC_ERR_INVALID_ARG),          # both force flags
+    (4, 4096, 20, 1e-6, 16, 0, 8, B.DS4HC_ERR_INVALID_ARG),         # unknown flag
+    (4, 4096, 20, 1e-6, 6, 0, 8, B.DS4HC_ERR_INVALID_ARG),          # two force flags
+    (4, 4096, 20, 1e-6, 10, 0, 8, B.DS4HC_ERR_INVALID_ARG),         # two force flags
+    (4, 8192, 20, 1e-6, 8, 0, 64, B.DS4HC_ERR_UNSUPPORTED),         # f32 row too long for tile
     (3, 4096, 20, 1e-6, 0, 0, 8, B.DS4HC_ERR_UNSUPPORTED),          # n = 3
     (8, 4096, 20, 1e-6, 0, 0, 8, B.DS4HC_ERR_UNSUPPORTED),          # n = 8
     (4, 4096, 1001, 1e-6, 0, 0, 8, B.DS4HC_ERR_UNSUPPORTED),        # iters too many

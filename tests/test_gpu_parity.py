@@ -17,7 +17,9 @@ from hc_testlib import (TOL, assert_close_rows, assert_coeffs, case_to_device, s
 
 pytestmark = pytest.mark.gpu
 
-FLAGS = {"default": 0, "rowres": B.DS4HC_FLAG_FORCE_ROWRES, "splitk": B.DS4HC_FLAG_FORCE_SPLITK}
+FLAGS = {"default": 0, "rowres": B.DS4HC_FLAG_FORCE_ROWRES, "tile": B.DS4HC_FLAG_FORCE_TILE,
+         "splitk": B.DS4HC_FLAG_FORCE_SPLITK}
+PATHS = ["default", "rowres", "tile", "splitk"]
 
 
 def torch_mod():
@@ -55,19 +57,19 @@ def check_full(case, got, what):
 
 # ------------------------------------------------------------------ workloads, every element
 
-@pytest.mark.parametrize("path", ["default", "rowres", "splitk"])
+@pytest.mark.parametrize("path", PATHS)
 def test_single_token(path):
     case = wl.make_single(0)
     check_full(case, run_fused(case, FLAGS[path]), f"single/{path}")
 
 
-@pytest.mark.parametrize("path", ["default", "rowres", "splitk"])
+@pytest.mark.parametrize("path", PATHS)
 def test_verify_batch(path):
     case = wl.make_verify(0)
     check_full(case, run_fused(case, FLAGS[path]), f"verify/{path}")
 
 
-@pytest.mark.parametrize("path", ["default", "rowres", "splitk"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("T", [37, 67])
 def test_prefill_reduced_T(path, T):
     """Prefill shape and value recipe (per-token log-uniform scales) at a T the
@@ -76,7 +78,7 @@ def test_prefill_reduced_T(path, T):
     check_full(case, run_fused(case, FLAGS[path]), f"prefill T={T}/{path}")
 
 
-@pytest.mark.parametrize("path", ["default", "rowres", "splitk"])
+@pytest.mark.parametrize("path", PATHS)
 def test_stress_reduced_T(path):
     """Stress recipe (bf16, residual logit std ~20, 5 % zero rows) at T = 41, d = 7168:
     d is not a multiple of the row-resident chunk, so the last chunk is ragged."""
@@ -91,12 +93,14 @@ def test_stress_reduced_T(path):
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 @pytest.mark.parametrize("n,d", [(1, 8), (1, 1032), (2, 264), (2, 4096), (4, 8), (4, 2056),
                                  (4, 16384)])
-@pytest.mark.parametrize("path", ["rowres", "splitk"])
+@pytest.mark.parametrize("path", ["rowres", "tile", "splitk"])
 def test_shapes(dtype, n, d, path):
+    V = 4 if dtype == wl.F32 else 8
     cap = (7 if dtype == wl.F32 else 5) if n == 4 else 8
-    rowres_limit = cap * 256 * (4 if dtype == wl.F32 else 8)
-    if path == "rowres" and d > rowres_limit:
+    if path == "rowres" and d > cap * 256 * V:
         pytest.skip("row too long for the row-resident kernel")
+    if path == "tile" and d > 8 * 4 * 32 * V:
+        pytest.skip("row too long for the tile kernel")
     case = wl.make_random(3 + n + d, 5, n, d, dtype)
     check_full(case, run_fused(case, FLAGS[path]), f"n={n} d={d} {dtype}/{path}")
 
