@@ -15,7 +15,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -28,21 +27,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "HC-op tokens/s and achieved HBM GB/s (% of peak) at T=4096, d=4096, n_hc=4"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["deepseek_v4_hyper_amd/csrc/hc_kernels.hip",
-                  "deepseek_v4_hyper_amd/csrc/hc_device.hpp",
-                  "deepseek_v4_hyper_amd/csrc/hc_launch.hpp"]
-KERNEL_NAME = {"default": "hc_rowres_kernel", "tile": "hc_tile_kernel", "rowres": "hc_rowres_kernel",
+KERNEL_NAME = {"default": "hc_tile_kernel", "tile": "hc_tile_kernel", "rowres": "hc_rowres_kernel",
                "splitk": "hc_partials_kernel+hc_finish_kernel"}
-COUNTERS_FILE = {"prefill": "profiles/hc_rowres_prefill_T4096_counters.json",
-                 "stress": "profiles/hc_rowres_stress_T16384_counters.json"}
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+COUNTERS_FILE = {"prefill": "profiles/hc_tile_prefill_T4096_counters.json",
+                 "stress": "profiles/hc_tile_stress_T16384_counters.json"}
 
 
 def algorithmic_bytes(T, n, d, state_bytes, with_coeffs=True):
@@ -114,14 +102,15 @@ def cpu_baseline(case, runs=3):
 
 
 def copy_calibration(nbytes=1 << 30):
-    """One plain device copy of known size, for scaling rocprofv3 FETCH/WRITE counters."""
+    """One plain elementwise copy of known size (read nbytes, write nbytes) as
+    the process's last kernel, for scaling rocprofv3 FETCH/WRITE counters."""
     import torch
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    b.copy_(a)
+    torch.mul(a, 1.0, out=b)
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e)
@@ -201,7 +190,8 @@ def main():
     sb = 4 if c0.dtype == wl.F32 else 2
     alg = algorithmic_bytes(T, n, d, sb)
     achieved = alg / (ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, kernel_source_hash()) if args.path in ("default", "rowres") \
+    from deepseek_v4_hyper_amd.counters import kernel_source_hash
+    traffic = load_traffic(args.workload, kernel_source_hash()) if args.path in ("default", "tile") \
         else None
     rec = {
         "metric": METRIC if args.workload == "prefill" else

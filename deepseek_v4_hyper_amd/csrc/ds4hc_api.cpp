@@ -71,9 +71,11 @@ struct Plan {
 };
 
 // Path for HC-pre / fused: split-K for small T (the fn weight dominates the
-// bytes and must be spread over many CUs), the one-token VALU kernel for
-// large T (measured faster than the two-token MFMA tile kernel on MI355X at
-// T = 4096 and 16384), split-K where a row is too long for it.
+// bytes and must be spread over many CUs), the persistent MFMA tile kernel
+// for large T (measured on MI355X at n = 4: 184 us against 280 us for the
+// one-token VALU kernel at T = 4096, d = 4096 float32, and 691 us against
+// 1333 us at T = 16384, d = 7168 bfloat16), then the VALU kernel, then
+// split-K where a row is too long for either.
 // Returns UNSUPPORTED if a forced path cannot take the shape or a launch
 // would not fit.
 ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *out) {
@@ -93,13 +95,13 @@ ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *o
     } else if (T <= SPLITK_MAX_T) {
         path = ds4hc::PATH_SPLITK;
     } else {
-        path = fits_rowres ? ds4hc::PATH_ROWRES : fits_tile ? ds4hc::PATH_TILE : ds4hc::PATH_SPLITK;
+        path = fits_tile ? ds4hc::PATH_TILE : fits_rowres ? ds4hc::PATH_ROWRES : ds4hc::PATH_SPLITK;
     }
     Plan pl{path, 0, 0};
     if (path == ds4hc::PATH_ROWRES) {
         if ((uint64_t)T * 256u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
     } else if (path == ds4hc::PATH_TILE) {
-        if ((uint64_t)(T + 1) / 2 * 256u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
+        // persistent grid: at most one workgroup per CU, whatever T is
     } else {
         pl.P = ds4hc::splitk_chunks(n, d, dt);
         const uint64_t tg = (uint64_t)(T + 3) / 4;

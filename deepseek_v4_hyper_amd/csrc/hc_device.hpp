@@ -152,6 +152,51 @@ __device__ __forceinline__ float sinkhorn_lane(float z, int iters) {
     return m;
 }
 
+// DPP lane exchange of a float (quad permutes and row rotations).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Same result as sinkhorn_lane, with the lane exchanges done by DPP (no LDS
+// crossbar traffic). Row reductions (over j) are xor butterflies inside a
+// quad; column reductions (over i) for n = 4 rotate the 16-lane row by 8 and
+// then 4 lanes. Every lane of a row (column) ends with the same sum bits.
+template <int N>
+__device__ __forceinline__ float sinkhorn_lane_dpp(float z, int iters) {
+    static_assert(N == 1 || N == 2 || N == 4, "n_hc");
+    if constexpr (N == 1) {
+        float m = expf(z - z);
+        for (int it = 0; it < iters; ++it) {
+            m = m / m;
+            m = m / m;
+        }
+        return m;
+    } else {
+        constexpr int XOR1 = 0xB1, XOR2 = 0x4E, ROR4 = 0x124, ROR8 = 0x128;
+        float mx = z;
+        mx = fmaxf(mx, dpp_mov<XOR1>(mx));
+        if constexpr (N == 4) mx = fmaxf(mx, dpp_mov<XOR2>(mx));
+        float m = expf(z - mx);
+        for (int it = 0; it < iters; ++it) {
+            float rs = m + dpp_mov<XOR1>(m);
+            if constexpr (N == 4) rs = rs + dpp_mov<XOR2>(rs);
+            m = m / rs;
+            float cs;
+            if constexpr (N == 4) {
+                // rows i and i+2 first: then every lane of a column adds the
+                // same two partial sums, so all four hold identical bits.
+                cs = m + dpp_mov<ROR8>(m);
+                cs = cs + dpp_mov<ROR4>(cs);
+            } else {
+                cs = m + dpp_mov<XOR2>(m);
+            }
+            m = m / cs;
+        }
+        return m;
+    }
+}
+
 __device__ __forceinline__ float logistic(float v) { return 1.0f / (1.0f + expf(-v)); }
 
 }  // namespace ds4hc

@@ -24,6 +24,8 @@
 #include "hc_device.hpp"
 #include "hc_launch.hpp"
 
+#include <atomic>
+
 #include <tuple>
 #include <utility>
 
@@ -194,41 +196,37 @@ __global__ __launch_bounds__(ROWRES_THREADS) void hc_rowres_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// MFMA tile kernel: two tokens per 256-thread workgroup, rows kept in
-// registers, the fn matvec on v_mfma_f32_4x4x4_16b_f16.
+// MFMA tile kernel: persistent, one 512-thread workgroup per CU striding over
+// tiles of four tokens; the tile's rows are kept in registers and the fn
+// matvec runs on v_mfma_f32_4x4x4_16b_f16.
 //
-// The fn projection z = W . x~ (x~ = x / r) is a [24 x K] . [K x 2] product
-// per workgroup. One 4x4x4_16b instruction is 16 independent 4x4x4 products
-// (block b = lane / 4): A_b = 4 rows of W x 4 consecutive k, B_b = 4 k x 4
-// columns, where the columns are (token 0 hi, token 0 lo, token 1 hi,
-// token 1 lo). x~ is split exactly into f16 hi + lo (hi = f16(x~),
-// lo = f16(x~ - hi)), so hi + lo carries x~ to ~2^-23 relative and the
-// products are exact; accumulation is fp32. |x~| <= sqrt(K), so f16 cannot
-// overflow. Lane 4b + 2t + p holds V state elements of token t (p = 0 the
-// first, p = 1 the second V of block b's 2V columns); a quad DPP swap hands
-// each lane the hi or lo half its column needs from its partner.
+// The fn projection of a tile is a [m x K] . [K x 4] product. One
+// 4x4x4_16b instruction is 16 independent 4x4x4 products (block b = lane/4):
+// A_b = 4 rows of W x 4 consecutive k, B_b = those 4 k x the 4 tokens. Lane
+// 4b + t supplies token t's B column and W row t of the group's A. x~ = x/r
+// is split exactly into f16 hi + lo (hi = f16(x~), lo = f16(x~ - hi)); hi and
+// lo are two MFMAs on the same A accumulating into one result, so hi + lo
+// carries x~ to ~2^-23 relative, products are exact and accumulation is
+// fp32. |x~| <= sqrt(K), so f16 cannot overflow. Each W element fetched from
+// L2 feeds all four tokens.
 //
-// Column step j of wave w covers STEP = 32*V columns of every stream:
-// columns (w + 4j)*STEP + b*2V + p*V .. +V-1, so every lane holds all n
-// streams of its columns and the post update needs no data exchange.
+// W (the same for every tile) streams from L2 through a ring of unit-sized
+// slots in LDS, one ring per wave, filled by direct buffer->LDS loads that
+// run RING - 1 units ahead of the MFMAs and straight on into the next tile.
+// The next tile's rows are loaded into each column step's registers as soon
+// as the post update has consumed them, so HBM reads of tile k+1 overlap the
+// reductions, the Sinkhorn and the stores of tile k.
+//
+// Column step j of wave w covers STEP = 16*V columns of every stream:
+// columns (w + 8j)*STEP + b*V .. +V-1 for token t = lane % 4, so every lane
+// holds all n streams of its columns and the post update needs no exchange.
 // ---------------------------------------------------------------------------
-// Opaque register barrier: the compiler must assume the packed vector changed,
-// so it re-derives float32 values from it instead of keeping unpacked copies of
-// a whole register-resident row live across phases (which spills to scratch).
-template <int DT>
-__device__ __forceinline__ void launder(StateVec<DT> &v) {
-    asm volatile("" : "+v"(v.raw.x), "+v"(v.raw.y), "+v"(v.raw.z), "+v"(v.raw.w));
-}
-
-// Word 3 of a gfx9-family buffer resource descriptor (32-bit data format,
-// raw addressing); loads at or past num_records return zero.
-constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int uint2_t __attribute__((ext_vector_type(2)));
 
-constexpr int TILE_TOKENS = 2;
-constexpr int TILE_THREADS = 256;
+constexpr int TILE_TOKENS = 4;
+constexpr int TILE_THREADS = 512;
 constexpr int TILE_WAVES = TILE_THREADS / 64;
 
 // Opaque register barrier on a 4 x f16 value: later uses see these exact bits.
@@ -236,14 +234,6 @@ __device__ __forceinline__ void pin_half4(half4_t &v) {
     uint2_t u = __builtin_bit_cast(uint2_t, v);
     asm volatile("" : "+v"(u.x), "+v"(u.y));
     v = __builtin_bit_cast(half4_t, u);
-}
-
-// Exchange a 4 x f16 value with the partner lane (lane ^ 1) of the quad.
-__device__ __forceinline__ half4_t quad_swap(half4_t v) {
-    uint2_t u = __builtin_bit_cast(uint2_t, v);
-    u.x = (unsigned)__builtin_amdgcn_mov_dpp((int)u.x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-    u.y = (unsigned)__builtin_amdgcn_mov_dpp((int)u.y, 0xB1, 0xF, 0xF, false);
-    return __builtin_bit_cast(half4_t, u);
 }
 
 // Sub-block sb (4 consecutive float16) of a packed W slice, as an MFMA operand.
@@ -260,114 +250,290 @@ __device__ __forceinline__ half4_t half_sub4(const HalfVec<V> &h, int sb) {
     return __builtin_bit_cast(half4_t, u);
 }
 
+// Opaque register barrier: the compiler must assume the packed vector changed,
+// so it re-derives float32 values from it instead of keeping unpacked copies of
+// a whole register-resident row live across phases (which spills to scratch).
+template <int DT>
+__device__ __forceinline__ void launder(StateVec<DT> &v) {
+    asm volatile("" : "+v"(v.raw.x), "+v"(v.raw.y), "+v"(v.raw.z), "+v"(v.raw.w));
+}
+
+// Word 3 of a gfx9-family buffer resource descriptor (32-bit data format,
+// raw addressing); loads at or past num_records return zero.
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
+
+// A byte offset past any buffer this library describes: loads through it
+// return zero and stores through it are dropped. Masking by offset keeps
+// every load and store unconditional (no branches around memory operations,
+// which would make the compiler drain all outstanding loads at the joins).
+constexpr int OOB_OFFSET = 0x7FFFFFF0;
+
+// W for one (column step, stream) unit: V float16 of row 4g + lane%4 per group.
+template <int V, int G>
+__device__ __forceinline__ void load_w_unit(HalfVec<V> (&w)[G], __amdgpu_buffer_rsrc_t rsrc,
+                                            int voff, int soff_base, int soff_group) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int soff = soff_base + g * soff_group;
+        if constexpr (V == 4) {
+            const uint2_t u = __builtin_bit_cast(
+                uint2_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, 0));
+            w[g].raw = make_uint2(u.x, u.y);
+        } else {
+            w[g].raw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
+        }
+    }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             BUFFER_RSRC_WORD3);
+}
+
+// 16-byte state vector through a buffer descriptor (zero past num_records).
+template <int DT>
+__device__ __forceinline__ StateVec<DT> buf_load_vec(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    StateVec<DT> v;
+    if constexpr (DT == DT_F32)
+        v.raw = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                            __uint_as_float(u.w));
+    else
+        v.raw = u;
+    return v;
+}
+
+// Store V float32 values as one 16-byte state vector (one RNE rounding for bf16);
+// stores past num_records are dropped. The whole offset goes in the vector
+// offset and the scalar offset is the constant 0: with an SGPR scalar offset
+// the compiler assumes the 128-bit store-data hazard cannot occur and lets
+// the next VALU instruction overwrite the data VGPRs at once, and on gfx950
+// that corrupted the first dword of the stored vector.
+template <int DT>
+__device__ __forceinline__ void buf_store_vec(__amdgpu_buffer_rsrc_t r, int voff, const float *f) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 u;
+    if constexpr (DT == DT_F32) {
+        u = (u32x4){__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                    __float_as_uint(f[3])};
+    } else {
+        u = (u32x4){f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16),
+                    f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16),
+                    f32_to_bf16_bits(f[4]) | (f32_to_bf16_bits(f[5]) << 16),
+                    f32_to_bf16_bits(f[6]) | (f32_to_bf16_bits(f[7]) << 16)};
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, voff, 0, 0);
+}
+
+// Per-wave ring of weight units in LDS, filled by direct buffer->LDS loads.
+constexpr int TILE_RING_BYTES = 18 * 1024;  // per wave; 8 waves -> 144 KiB of the 160 KiB LDS
+
+// Issue one direct buffer->LDS load of 16 bytes per lane: lane l's bytes land
+// at lds_base + 16*l. Written as inline assembly so the compiler does not
+// track it: its conservative handling of LDS DMA would drain every load in
+// flight before each LDS read. Completion is waited for explicitly with
+// wait_vm_at_most() before the data is read.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base,
+                                          int voff, int soff) {
+    // M0 holds the LDS destination; one wait state must separate its write
+    // from an LDS-DMA load that reads it. M0 is reserved to the compiler, so
+    // the asm saves and restores it rather than declaring it clobbered.
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding.
+// Vector memory operations complete in issue order, so every operation older
+// than the last n is then complete.
+template <int n>
+__device__ __forceinline__ void wait_vm_at_most() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] at [15:14]
+    constexpr int enc = (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+    asm volatile("s_waitcnt %0" : : "n"(enc) : "memory");
+}
+
+// Sum over the 16 lanes of a DPP row that share lane % 4 (blocks of a row):
+// rotations by 4 and 8 lanes.
+__device__ __forceinline__ float row_sum_by4(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    return v;
+}
+
 template <int N, int DT, int CS, int MODE>
-__global__ __launch_bounds__(TILE_THREADS, 2) void hc_tile_kernel(
+__global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
     int d, int T, float eps, int iters, const void *__restrict__ X, const uint16_t *__restrict__ W,
     const float *__restrict__ bias, const void *__restrict__ layer_out, void *__restrict__ layer_in,
     float *__restrict__ coeffs, float *__restrict__ logits, void *X_out) {
     constexpr int V = StateVec<DT>::V;
     constexpr int M = n_logits(N);
-    constexpr int G = (M + 3) / 4;  // groups of 4 W rows
-    constexpr int SB = V / 4;       // 4-element sub-blocks per lane vector
-    constexpr int STEP = 32 * V;    // columns per step
+    constexpr int G = (M + 3) / 4;   // groups of 4 W rows
+    constexpr int SB = V / 4;        // 4-element k-blocks per lane vector
+    constexpr int STEP = 16 * V;     // columns per step
+    constexpr int U = CS * N;        // (column step, stream) units per wave and tile
+    constexpr int ROWB = STEP * 2;   // bytes of one W row within a unit
+    constexpr int UNIT = 4 * G * ROWB;
+    constexpr int LOADS = (UNIT + 1023) / 1024;  // 16-byte-per-lane loads per unit
+    constexpr int SLOT = LOADS * 1024;
+    constexpr int RING_FIT = TILE_RING_BYTES / SLOT;
+    // At most U slots: the ring then always holds consecutive units of one
+    // tile or the next, which is what the refill below assumes.
+    constexpr int RING_CAP = RING_FIT > 8 ? 8 : RING_FIT;
+    constexpr int RING = RING_CAP < U ? RING_CAP : U;
+    constexpr int SBYTES = DT == DT_F32 ? 4 : 2;
+    static_assert(RING >= 1 && RING * SLOT <= TILE_RING_BYTES, "weight ring");
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // readfirstlane makes the wave index (and every offset built from it) a
     // scalar the compiler can put in the buffer loads' scalar offset field.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int blk = lane >> 2;
-    const int t = (lane >> 1) & 1;
-    const int p = lane & 1;
-    const int row4 = lane & 3;
-    const size_t tok = (size_t)blockIdx.x * TILE_TOKENS + t;
-    const bool tok_ok = tok < (size_t)T;
     const size_t K = (size_t)N * d;
+    const int ntiles = (T + TILE_TOKENS - 1) / TILE_TOKENS;
 
+    __shared__ __attribute__((aligned(16))) unsigned char wring[TILE_WAVES][RING][SLOT];
     __shared__ float ssr[TILE_WAVES][TILE_TOKENS];
-    __shared__ float zred[TILE_WAVES][4][G * 4];
+    __shared__ float zred[TILE_WAVES][TILE_TOKENS][G * 4];
     __shared__ float zs[TILE_TOKENS][M];
     __shared__ float cf[TILE_TOKENS][M];
 
-    // ---- phase 1: the two rows into registers, sum of squares ----
-    StateVec<DT> xv[N][CS];
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < CS; ++j) {
-        const int c0 = (wave + TILE_WAVES * j) * STEP + blk * 2 * V + p * V;
-        const bool ok = tok_ok && c0 < d;
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            xv[i][j] = ok ? load_vec<DT>(X, tok * K + (size_t)i * d + c0) : zero_vec<DT>();
-    }
-#pragma unroll
-    for (int j = 0; j < CS; ++j)
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const float x = vec_get<DT>(xv[i][j], e);
-                ss = fmaf(x, x, ss);
-            }
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 4, 64);
-    ss += __shfl_xor(ss, 8, 64);
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    if (lane == 0 || lane == 2) ssr[wave][t] = ss;
-    __syncthreads();
-    float sst = ssr[0][t];
-#pragma unroll
-    for (int w = 1; w < TILE_WAVES; ++w) sst += ssr[w][t];
-    const float inv_r = 1.0f / sqrtf(sst / (float)K + eps);
-
-    // ---- phase 2: fn matvec on MFMA ----
+    // ---- weight units: unit u = (column step u / N of this wave, stream u % N).
+    // Load q of a unit: lane l fetches bytes [p, p+16) of the unit's [4G rows][STEP
+    // columns] f16 block, p = 1024 q + 16 l: row p / ROWB, byte p % ROWB of the
+    // row's slice. ROWB divides 1024, so the column is the same for every q
+    // and load q is row offset q * 1024 / ROWB further down. Rows at or past M
+    // lie past the end of W, so the buffer descriptor turns them into zeros.
+    static_assert(1024 % ROWB == 0, "weight unit rows");
+    constexpr int QROWS = 1024 / ROWB;
     const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(W), (short)0, (int)((size_t)M * K * 2), BUFFER_RSRC_WORD3);
-    // W row 4g + row4 of every group through one descriptor: a per-lane byte
-    // offset plus a wave-uniform offset per (group, stream, step). Padding rows
-    // (>= M, when M % 4 != 0) fall past the end of W and read as zero.
-    const int w_voff = (int)((row4 * K + blk * 2 * V) * 2);
+    const int row_bytes = (int)(K * 2);
+    const uint32_t ring_base = (uint32_t)(uintptr_t)&wring[wave][0][0];
+    auto unit_step = [&](int u) { return wave + TILE_WAVES * (u / N); };
+    // wlane = this lane's offset within a unit's first load, wcol its column.
+    auto issue_unit = [&](int u, int slot, int dd, int wlane, int wcol) {
+        const int soff = ((u % N) * dd + unit_step(u) * STEP) * 2;
+        const bool ok = wcol < dd - unit_step(u) * STEP;
 #pragma unroll
-    for (int j = 0; j < CS; ++j)
+        for (int q = 0; q < LOADS; ++q) {
+            const int voff = ok ? wlane + q * QROWS * row_bytes : OOB_OFFSET;
+            lds_dma16(wrsrc, ring_base + (uint32_t)(slot * SLOT + q * 1024), voff, soff);
+        }
+    };
+    auto lane_wlane = [&](int ln) { return (16 * ln / ROWB) * row_bytes + (16 * ln) % ROWB; };
+    auto lane_wcol = [&](int ln) { return ((16 * ln) % ROWB) / 2; };
+
+    // the first tile's first RING units, before anything else
 #pragma unroll
-        for (int i = 0; i < N; ++i) launder<DT>(xv[i][j]);
-    float4_t acc[G];
+    for (int u = 0; u < RING; ++u) issue_unit(u, u, d, lane_wlane(lane), lane_wcol(lane));
+
+    auto tile_rsrc = [&](const void *base, size_t row_elems, int tile) {
+        const size_t tile0 = (size_t)tile * TILE_TOKENS;
+        const size_t ntok = min((size_t)TILE_TOKENS, (size_t)T - tile0);
+        return make_rsrc((const char *)base + tile0 * row_elems * SBYTES,
+                         (uint32_t)(ntok * row_elems * SBYTES));
+    };
+
+    // ---- the first tile's rows into registers ----
+    StateVec<DT> xv[N][CS];
+    {
+        const __amdgpu_buffer_rsrc_t xr = tile_rsrc(X, K, blockIdx.x);
+        const int bv = (lane >> 2) * V;
+        const int x_voff = ((lane & 3) * (int)K + bv) * SBYTES;
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < CS; ++j) {
+            const int cs = wave + TILE_WAVES * j;
+            const int voff = bv < d - cs * STEP ? x_voff : OOB_OFFSET;
 #pragma unroll
-    for (int j = 0; j < CS; ++j) {
-        const int cs = wave + TILE_WAVES * j;
-        if (cs * STEP >= d) break;  // wave-uniform
-        const int cb = cs * STEP + blk * 2 * V;  // first column of block b
-        const bool e_ok = cb < d, o_ok = cb + V < d;
+            for (int i = 0; i < N; ++i) xv[i][j] = buf_load_vec<DT>(xr, voff, (i * d + cs * STEP) * SBYTES);
+        }
+    }
+
+    int ring_pos = 0;  // ring slot of unit 0 of the current tile
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const bool has_next = tile + (int)gridDim.x < ntiles;
+        const size_t tile0 = (size_t)tile * TILE_TOKENS;
+        // Every per-lane offset and mask below is the same for every tile.
+        // Re-deriving them here from values hidden from the optimiser keeps it
+        // from hoisting them out of the loop into registers that stay live for
+        // the whole kernel (they are a few integer operations per tile).
+        int dl = d, ln = lane;
+        asm volatile("" : "+s"(dl));  // (separate statements: an asm with any
+        asm volatile("" : "+v"(ln));  //  vector output counts as divergent)
+        const int tid_l = wave * 64 + ln;
+        const int blk = ln >> 2;
+        const int t = ln & 3;  // token of this lane's B column; also its A row in the group
+        const int bv = blk * V;  // this lane's first column within a column step
+        const int x_voff = (t * (int)K + bv) * SBYTES;
+        const int d_voff = (t * dl + bv) * SBYTES;
+        const int wlane = lane_wlane(ln), wcol = lane_wcol(ln);
+        const int wread = (t * ROWB + bv * 2);  // byte of row t's slice read by this lane
+
+        // ---- phase 1: sum of squares of the four rows ----
+        float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-            // A operands: W rows 4g + row4, columns cb .. cb + 2V - 1 of stream i
-            HalfVec<V> we[G], wo[G];
+        for (int j = 0; j < CS; ++j)
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float x = vec_get<DT>(xv[i][j], e);
+                    ss = fmaf(x, x, ss);
+                }
+        ss += __shfl_xor(ss, 4, 64);
+        ss += __shfl_xor(ss, 8, 64);
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (ln < TILE_TOKENS) ssr[wave][ln] = ss;
+        __syncthreads();
+        float sst = ssr[0][t];
+#pragma unroll
+        for (int w = 1; w < TILE_WAVES; ++w) sst += ssr[w][t];
+        const float inv_r = 1.0f / sqrtf(sst / (float)K + eps);
+
+        // ---- phase 2: fn matvec on MFMA, weights from the LDS ring ----
+        float4_t acc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < CS; ++j)
+#pragma unroll
+            for (int i = 0; i < N; ++i) launder<DT>(xv[i][j]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int slot = ring_pos + u % RING;
+            slot = slot >= RING ? slot - RING : slot;
+            // Unit u's loads are complete once no more vector-memory
+            // operations are outstanding than were issued after them: the
+            // refills of the next RING - 1 units (some of them the next
+            // tile's). Anything else issued since only makes this stricter.
+            wait_vm_at_most<LOADS * (RING - 1)>();
+            HalfVec<V> w[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const int soff = (int)((4 * g * K + (size_t)i * d + (size_t)cs * STEP) * 2);
-                if constexpr (V == 4) {
-                    uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, soff, 0));
-                    if (!e_ok) u = make_uint4(0u, 0u, 0u, 0u);
-                    we[g].raw = make_uint2(u.x, u.y);
-                    wo[g].raw = make_uint2(u.z, u.w);
-                } else {
-                    uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, soff, 0));
-                    uint4 b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff + 16, soff, 0));
-                    if (!e_ok) a = make_uint4(0u, 0u, 0u, 0u);
-                    if (!o_ok) b = make_uint4(0u, 0u, 0u, 0u);
-                    we[g].raw = a;
-                    wo[g].raw = b;
-                }
+                const unsigned char *src = &wring[wave][slot][4 * g * ROWB + wread];
+                if constexpr (V == 4)
+                    w[g].raw = *reinterpret_cast<const uint2 *>(src);
+                else
+                    w[g].raw = *reinterpret_cast<const uint4 *>(src);
             }
-            half4_t hi[SB], lo[SB], rcv[SB];
+            const StateVec<DT> &xvu = xv[u % N][u / N];
+            half4_t hi[SB], lo[SB];
 #pragma unroll
             for (int sb = 0; sb < SB; ++sb) {
                 float xt[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    xt[e] = vec_get<DT>(xv[i][j], 4 * sb + e) * inv_r;
+                    xt[e] = vec_get<DT>(xvu, 4 * sb + e) * inv_r;
                     hi[sb][e] = (_Float16)xt[e];
                 }
                 // lo must be formed from the very bits the MFMA consumes as hi:
@@ -377,126 +543,140 @@ __global__ __launch_bounds__(TILE_THREADS, 2) void hc_tile_kernel(
                 pin_half4(hi[sb]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) lo[sb][e] = (_Float16)(xt[e] - (float)hi[sb][e]);
-                rcv[sb] = quad_swap(p ? hi[sb] : lo[sb]);
             }
 #pragma unroll
-            for (int sb = 0; sb < SB; ++sb) {
-                const half4_t be = p ? rcv[sb] : hi[sb];  // block columns cb + 4sb ..
-                const half4_t bo = p ? lo[sb] : rcv[sb];  // block columns cb + V + 4sb ..
+            for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-                for (int g = 0; g < G; ++g)
-                    acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(half_sub4<V>(we[g], sb), be,
-                                                                acc[g], 0, 0, 0);
+                for (int g = 0; g < G; ++g) {
+                    const half4_t a = half_sub4<V>(w[g], sb);
+                    acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, hi[sb], acc[g], 0, 0, 0);
+                    acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, lo[sb], acc[g], 0, 0, 0);
+                }
+            // Refill this slot once this wave's reads of it are done: unit
+            // u + RING of this tile, or of the next one. W is the same for
+            // every tile, so the last tile refills too (the units go unused);
+            // that keeps the count of loads in flight the same for every unit.
+            const int nu = u + RING;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue_unit(nu < U ? nu : nu - U, slot, dl, wlane, wcol);
+        }
+        ring_pos = (ring_pos + U) % RING;
+
+        // layer_out for the post update: issued now, consumed after the reductions
+        // and the Sinkhorn, whose latency it hides.
+        StateVec<DT> lov[CS];
+        if constexpr (MODE == MODE_FUSED) {
+            const __amdgpu_buffer_rsrc_t lr = tile_rsrc(layer_out, (size_t)d, tile);
 #pragma unroll
-                for (int g = 0; g < G; ++g)
-                    acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(half_sub4<V>(wo[g], sb), bo,
-                                                                acc[g], 0, 0, 0);
+            for (int j = 0; j < CS; ++j) {
+                const int cs = wave + TILE_WAVES * j;
+                const int voff = bv < dl - cs * STEP ? d_voff : OOB_OFFSET;
+                lov[j] = buf_load_vec<DT>(lr, voff, cs * STEP * SBYTES);
             }
         }
-    }
 
-    // layer_out for the post update: issued now, consumed after the reductions
-    // and the Sinkhorn, whose latency it hides.
-    StateVec<DT> lov[CS];
-    if constexpr (MODE == MODE_FUSED) {
+        // ---- phase 3: sum the 16 blocks (DPP within rows, then LDS), then the waves ----
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = row_sum_by4(acc[g][r]);
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                if (ln < TILE_TOKENS) zred[wave][ln][4 * g + r] = v;
+            }
+        __syncthreads();
+        if (tid_l < TILE_TOKENS * M) {
+            const int tt = tid_l / M, row = tid_l % M;
+            float s = zred[0][tt][row];
+#pragma unroll
+            for (int w = 1; w < TILE_WAVES; ++w) s += zred[w][tt][row];
+            const float z = s + bias[row];
+            zs[tt][row] = z;
+            const size_t tk = tile0 + tt;
+            if (logits && tk < (size_t)T) logits[tk * M + row] = z;
+        }
+        __syncthreads();
+
+        // ---- phase 4: gates and Sinkhorn for the four tokens (wave 0) ----
+        if (wave == 0) {
+            constexpr int NN = N * N;
+            const int grp = ln / NN, e = ln % NN, tt = grp % TILE_TOKENS;
+            const float h = sinkhorn_lane_dpp<N>(zs[tt][2 * N + e], iters);
+            const size_t tk = tile0 + tt;
+            if (grp < TILE_TOKENS) {
+                cf[tt][2 * N + e] = h;
+                if (coeffs && tk < (size_t)T) coeffs[tk * M + 2 * N + e] = h;
+            }
+            if (ln < TILE_TOKENS * 2 * N) {
+                const int gt = ln / (2 * N), idx = ln % (2 * N);
+                const float gv = logistic(zs[gt][idx]);
+                cf[gt][idx] = gv;
+                const size_t gk = tile0 + gt;
+                if (coeffs && gk < (size_t)T) coeffs[gk * M + idx] = gv;
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 5: pre-mix and post update from the registers; the next
+        // tile's rows are loaded into each step's registers as soon as they are free ----
+        float pre[N], post[N], H[N][N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            pre[i] = cf[t][i];
+            post[i] = cf[t][N + i];
+#pragma unroll
+            for (int j = 0; j < N; ++j) H[i][j] = cf[t][2 * N + i * N + j];
+        }
+#pragma unroll
+        for (int j = 0; j < CS; ++j)
+#pragma unroll
+            for (int i = 0; i < N; ++i) launder<DT>(xv[i][j]);
+        const __amdgpu_buffer_rsrc_t lir = tile_rsrc(layer_in, (size_t)d, tile);
+        const __amdgpu_buffer_rsrc_t xor_ = tile_rsrc(X_out, K, tile);
+        const __amdgpu_buffer_rsrc_t xnext = tile_rsrc(X, K, has_next ? tile + (int)gridDim.x : tile);
 #pragma unroll
         for (int j = 0; j < CS; ++j) {
-            const int c0 = (wave + TILE_WAVES * j) * STEP + blk * 2 * V + p * V;
-            lov[j] = (tok_ok && c0 < d) ? load_vec<DT>(layer_out, tok * d + c0) : zero_vec<DT>();
-        }
-    }
-
-    // ---- phase 3: sum the 16 blocks, then the waves, in a fixed order ----
+            const int cs = wave + TILE_WAVES * j;
+            const bool col_ok = bv < dl - cs * STEP;
+            float x[N][V];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+            for (int i = 0; i < N; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float v = acc[g][r];
-            v += __shfl_xor(v, 4, 64);
-            v += __shfl_xor(v, 8, 64);
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            if (lane < 4) zred[wave][lane][4 * g + r] = v;
-        }
-    __syncthreads();
-    if (tid < TILE_TOKENS * M) {
-        const int tt = tid / M, row = tid % M;
-        float s = zred[0][2 * tt][row] + zred[0][2 * tt + 1][row];
+                for (int e = 0; e < V; ++e) x[i][e] = vec_get<DT>(xv[i][j], e);
+            float li[V];
 #pragma unroll
-        for (int w = 1; w < TILE_WAVES; ++w) s += zred[w][2 * tt][row] + zred[w][2 * tt + 1][row];
-        const float z = s + bias[row];
-        zs[tt][row] = z;
-        const size_t tk = (size_t)blockIdx.x * TILE_TOKENS + tt;
-        if (logits && tk < (size_t)T) logits[tk * M + row] = z;
-    }
-    __syncthreads();
-
-    // ---- phase 4: gates and Sinkhorn for both tokens (wave 0) ----
-    if (wave == 0) {
-        constexpr int NN = N * N;
-        const int grp = lane / NN, e = lane % NN, tt = grp & 1;
-        const float h = sinkhorn_lane<N>(zs[tt][2 * N + e], iters);
-        const size_t tk = (size_t)blockIdx.x * TILE_TOKENS + tt;
-        if (grp < TILE_TOKENS) {
-            cf[tt][2 * N + e] = h;
-            if (coeffs && tk < (size_t)T) coeffs[tk * M + 2 * N + e] = h;
-        }
-        if (lane < TILE_TOKENS * 2 * N) {
-            const int gt = lane / (2 * N), idx = lane % (2 * N);
-            const float gv = logistic(zs[gt][idx]);
-            cf[gt][idx] = gv;
-            const size_t gk = (size_t)blockIdx.x * TILE_TOKENS + gt;
-            if (coeffs && gk < (size_t)T) coeffs[gk * M + idx] = gv;
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 5: pre-mix and post update from the registers ----
+            for (int e = 0; e < V; ++e) {
+                float s = pre[0] * x[0][e];
 #pragma unroll
-    for (int j = 0; j < CS; ++j)
+                for (int i = 1; i < N; ++i) s = fmaf(pre[i], x[i][e], s);
+                li[e] = s;
+            }
+            buf_store_vec<DT>(lir, col_ok ? d_voff + cs * STEP * SBYTES : OOB_OFFSET, li);
+            if constexpr (MODE == MODE_FUSED) {
 #pragma unroll
-        for (int i = 0; i < N; ++i) launder<DT>(xv[i][j]);
-    float pre[N], post[N], H[N][N];
+                for (int i = 0; i < N; ++i) {
+                    float o[V];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        pre[i] = cf[t][i];
-        post[i] = cf[t][N + i];
+                    for (int e = 0; e < V; ++e) {
+                        float s = H[i][0] * x[0][e];
 #pragma unroll
-        for (int j = 0; j < N; ++j) H[i][j] = cf[t][2 * N + i * N + j];
-    }
-#pragma unroll
-    for (int j = 0; j < CS; ++j) {
-        const int c0 = (wave + TILE_WAVES * j) * STEP + blk * 2 * V + p * V;
-        if (!tok_ok || c0 >= d) continue;
-        float x[N][V];
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-#pragma unroll
-            for (int e = 0; e < V; ++e) x[i][e] = vec_get<DT>(xv[i][j], e);
-        float li[V];
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-            float s = pre[0] * x[0][e];
-#pragma unroll
-            for (int i = 1; i < N; ++i) s = fmaf(pre[i], x[i][e], s);
-            li[e] = s;
-        }
-        store_vec<DT>(layer_in, tok * d + c0, li);
-        if constexpr (MODE == MODE_FUSED) {
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                float o[V];
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    float s = H[i][0] * x[0][e];
-#pragma unroll
-                    for (int jj = 1; jj < N; ++jj) s = fmaf(H[i][jj], x[jj][e], s);
-                    o[e] = fmaf(post[i], vec_get<DT>(lov[j], e), s);
+                        for (int jj = 1; jj < N; ++jj) s = fmaf(H[i][jj], x[jj][e], s);
+                        o[e] = fmaf(post[i], vec_get<DT>(lov[j], e), s);
+                    }
+                    buf_store_vec<DT>(xor_, col_ok ? x_voff + (i * d + cs * STEP) * SBYTES : OOB_OFFSET, o);
                 }
-                store_vec<DT>(X_out, tok * K + (size_t)i * d + c0, o);
+            }
+            {
+                // (zeros past the last tile: no branch around the loads)
+                const int voff = col_ok && has_next ? x_voff : OOB_OFFSET;
+#pragma unroll
+                for (int i = 0; i < N; ++i) xv[i][j] = buf_load_vec<DT>(xnext, voff, (i * dl + cs * STEP) * SBYTES);
             }
         }
     }
+    // no load into this workgroup's LDS may still be in flight when it ends
+    wait_vm_at_most<0>();
 }
 
 // ---------------------------------------------------------------------------
@@ -716,9 +896,37 @@ static hipError_t launch_rowres_n(int cq, const FusedArgs &a, hipStream_t s) {
 #undef DS4HC_ROWRES_CASE
 }
 
+// Compute units of the current device, looked up once per device.
+static hipError_t device_cu_count(int *cus) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return hipSuccess;
+        }
+    }
+    int c = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (c <= 0) return hipErrorInvalidDevice;
+    if (dev >= 0 && dev < 64) cache[dev].store(c, std::memory_order_relaxed);
+    *cus = c;
+    return hipSuccess;
+}
+
 template <int N, int DT, int MODE>
 static hipError_t launch_tile_n(int cs, const FusedArgs &a, hipStream_t s) {
-    const dim3 grid((unsigned)((a.T + TILE_TOKENS - 1) / TILE_TOKENS)), block(TILE_THREADS);
+    // Persistent: one workgroup per compute unit (the weight ring takes most
+    // of a CU's LDS, so no second one would fit), each striding over tiles.
+    int cus = 0;
+    const hipError_t e = device_cu_count(&cus);
+    if (e != hipSuccess) return e;
+    const int64_t ntiles = (a.T + TILE_TOKENS - 1) / TILE_TOKENS;
+    const dim3 grid((unsigned)(ntiles < cus ? ntiles : cus)), block(TILE_THREADS);
 #define DS4HC_TILE_CASE(CS)                                                                      \
     case CS:                                                                                     \
         return launch_kernel(hc_tile_kernel<N, DT, CS, MODE>, grid, block, s, a.d, (int)a.T,     \
@@ -781,7 +989,7 @@ int rowres_max_chunks(int n, int dt) { return rowres_cap(n, dt); }
 
 int tile_steps(int d, int dt) {
     const int V = dt == DT_F32 ? 4 : 8;
-    const int steps = (d + 32 * V - 1) / (32 * V);
+    const int steps = (d + 16 * V - 1) / (16 * V);
     return (steps + TILE_WAVES - 1) / TILE_WAVES;
 }
 

@@ -105,6 +105,45 @@ def test_shapes(dtype, n, d, path):
     check_full(case, run_fused(case, FLAGS[path]), f"n={n} d={d} {dtype}/{path}")
 
 
+# ------------------------------------------------------------------ persistent tile grid
+
+def _cu_count():
+    return torch_mod().cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("n,d,dtype", [(4, 512, wl.F32), (4, 1024, wl.BF16), (2, 264, wl.F32),
+                                       (1, 1032, wl.BF16)])
+def test_tile_several_tiles_per_workgroup(n, d, dtype):
+    """T = 8 * CUs + 3: the persistent grid has one workgroup per CU, so each
+    takes two tiles of four tokens and the first takes a third, ragged one of
+    three; the weight ring and the row prefetch carry over between tiles.
+    Every element is compared."""
+    T = 8 * _cu_count() + 3
+    case = wl.make_random(11 + n + d, T, n, d, dtype)
+    check_full(case, run_fused(case, FLAGS["tile"]), f"tile x3 n={n} d={d} {dtype}")
+
+
+def test_tile_prefill_recipe_several_tiles_in_place_and_pre():
+    """Prefill recipe at T = 8 * CUs + 3 on the tile path: fused against the
+    oracle on every element, in place (X_out = X) bitwise equal to out of
+    place, and HC-pre alone bitwise equal to the fused layer_in / coeffs."""
+    torch = torch_mod()
+    T = 8 * _cu_count() + 3
+    case = wl.make_prefill(12, T=T)
+    X, W, b, lo = case_to_device(case)
+    fl = FLAGS["tile"]
+    say(f"[gpu] tile path, prefill recipe T={T}: fused, in place, pre")
+    li, c, xo = B.ds4hc_fused(X, W, b, lo, flags=fl)
+    Xi = X.clone()
+    li2, c2, xo2 = B.ds4hc_fused(Xi, W, b, lo, flags=fl, X_out=Xi)
+    li3, c3, _ = B.ds4hc_pre(X, W, b, flags=fl)
+    torch.cuda.synchronize()
+    assert torch.equal(Xi, xo) and torch.equal(li2, li) and torch.equal(c2, c)
+    assert torch.equal(li3, li) and torch.equal(c3, c)
+    got = (torch_to_f64(li), c.cpu().numpy().astype(np.float64), torch_to_f64(xo))
+    check_full(case, got, f"prefill T={T}/tile")
+
+
 # ------------------------------------------------------------------ full-size workloads, sampled rows
 
 def _sampled_check(case, flags, nsample, extra_rows=()):
@@ -295,7 +334,7 @@ def test_logits_output_matches_oracle():
     case = wl.make_verify(9)
     X, W, b, _ = case_to_device(case)
     say("[gpu] ds4hc_pre logits")
-    for flags in (0, B.DS4HC_FLAG_FORCE_ROWRES):
+    for flags in (0, B.DS4HC_FLAG_FORCE_ROWRES, B.DS4HC_FLAG_FORCE_TILE):
         li, c, z = B.ds4hc_pre(X, W, b, flags=flags, want_logits=True)
         torch.cuda.synchronize()
         _, _, rz = oracle.pre(wl.state_to_f64(case.X, case.dtype), case.W, case.bias)
