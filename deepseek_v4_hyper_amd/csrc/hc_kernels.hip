@@ -369,6 +369,42 @@ __device__ __forceinline__ float row_sum_by4(float v) {
     return v;
 }
 
+// Sum over the 64 lanes that share lane % 4: rotations within each 16-lane
+// row, then the gfx950 row swaps (rows 0<->1, 2<->3, then halves), which move
+// data between rows in the VALU instead of through the LDS crossbar.
+__device__ __forceinline__ float wave_sum_by4(float v) {
+    v = row_sum_by4(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Largest biased float32 exponent among the N*V values of column step j,
+// from the raw bits (magnitudes compare as unsigned integers); NaN and Inf
+// give 255.
+template <int DT, int N, int CS>
+__device__ __forceinline__ int max_biased_exponent(const StateVec<DT> (&xv)[N][CS], int j) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t w[4] = {__builtin_bit_cast(uint32_t, xv[i][j].raw.x),
+                               __builtin_bit_cast(uint32_t, xv[i][j].raw.y),
+                               __builtin_bit_cast(uint32_t, xv[i][j].raw.z),
+                               __builtin_bit_cast(uint32_t, xv[i][j].raw.w)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (DT == DT_F32) {
+                m = max(m, w[q] & 0x7FFFFFFFu);
+            } else {
+                m = max(m, (w[q] & 0x7FFFu) << 16);
+                m = max(m, w[q] & 0x7FFF0000u);
+            }
+        }
+    }
+    return (int)(m >> 23);
+}
+
 template <int N, int DT, int CS, int MODE>
 __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
     int d, int T, float eps, int iters, const void *__restrict__ X, const uint16_t *__restrict__ W,
@@ -458,6 +494,10 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
         }
     }
 
+    // bias of the logit row this thread finishes in every tile, loaded once
+    // (a load inside the loop would make the compiler drain every load in flight)
+    const float bias_row = tid < TILE_TOKENS * M ? bias[tid % M] : 0.f;
+
     int ring_pos = 0;  // ring slot of unit 0 of the current tile
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const bool has_next = tile + (int)gridDim.x < ntiles;
@@ -478,36 +518,22 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
         const int wlane = lane_wlane(ln), wcol = lane_wcol(ln);
         const int wread = (t * ROWB + bv * 2);  // byte of row t's slice read by this lane
 
-        // ---- phase 1: sum of squares of the four rows ----
-        float ss = 0.f;
-#pragma unroll
-        for (int j = 0; j < CS; ++j)
-#pragma unroll
-            for (int i = 0; i < N; ++i)
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const float x = vec_get<DT>(xv[i][j], e);
-                    ss = fmaf(x, x, ss);
-                }
-        ss += __shfl_xor(ss, 4, 64);
-        ss += __shfl_xor(ss, 8, 64);
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        if (ln < TILE_TOKENS) ssr[wave][ln] = ss;
-        __syncthreads();
-        float sst = ssr[0][t];
-#pragma unroll
-        for (int w = 1; w < TILE_WAVES; ++w) sst += ssr[w][t];
-        const float inv_r = 1.0f / sqrtf(sst / (float)K + eps);
-
         // ---- phase 2: fn matvec on MFMA, weights from the LDS ring ----
+        // The projection runs on the raw rows and is normalised afterwards
+        // (z = (W . x) / r), so it does not wait for the whole tile to arrive:
+        // unit u needs only its own column step, and the rows of the next
+        // tile stream in while the MFMAs of its first units run. The f16
+        // split needs x scaled into f16 range: each lane keeps its own
+        // power-of-two scale 2^S, lowered (and its accumulators rescaled,
+        // exactly) when a column step brings a larger value. A lane's accumulators
+        // only ever hold its own B column (its token, its columns), so no
+        // other lane needs to agree on S. The sum of squares accumulates in
+        // the same pass.
         float4_t acc[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) acc[g] = (float4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < CS; ++j)
-#pragma unroll
-            for (int i = 0; i < N; ++i) launder<DT>(xv[i][j]);
+        int S = 140;  // |x| * 2^S < 2^14 for every x seen so far
+        float ss = 0.f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int slot = ring_pos + u % RING;
@@ -526,14 +552,34 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                 else
                     w[g].raw = *reinterpret_cast<const uint4 *>(src);
             }
+            if (u % N == 0) {
+                // the scale for the N units of this column step
+                const int eb = max_biased_exponent<DT, N>(xv, u / N);
+                // 2^(140 - eb) puts the largest |x| in [2^13, 2^14); for Inf or
+                // NaN the scale is tiny and Inf stays Inf, NaN stays NaN.
+                const int s_new = min(S, 140 - eb);
+                // Rescale unconditionally (by 2^0 when nothing changed): a
+                // branch here fragments the unrolled loop and costs registers.
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[g][r] = __builtin_amdgcn_ldexpf(acc[g][r], s_new - S);
+                S = s_new;
+            }
             const StateVec<DT> &xvu = xv[u % N][u / N];
+            float xr[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                xr[e] = vec_get<DT>(xvu, e);
+                ss = fmaf(xr[e], xr[e], ss);
+            }
             half4_t hi[SB], lo[SB];
 #pragma unroll
             for (int sb = 0; sb < SB; ++sb) {
                 float xt[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    xt[e] = vec_get<DT>(xvu, 4 * sb + e) * inv_r;
+                    xt[e] = __builtin_amdgcn_ldexpf(xr[4 * sb + e], S);
                     hi[sb][e] = (_Float16)xt[e];
                 }
                 // lo must be formed from the very bits the MFMA consumes as hi:
@@ -575,23 +621,32 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
             }
         }
 
-        // ---- phase 3: sum the 16 blocks (DPP within rows, then LDS), then the waves ----
+        // ---- phase 3: undo each lane's scale, sum the 16 blocks (DPP within
+        // rows, then across rows), then the waves; normalise by 1/r ----
+        ss = wave_sum_by4(ss);
+        float zsum[G][4];
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = row_sum_by4(acc[g][r]);
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                if (ln < TILE_TOKENS) zred[wave][ln][4 * g + r] = v;
-            }
+            for (int r = 0; r < 4; ++r) zsum[g][r] = wave_sum_by4(__builtin_amdgcn_ldexpf(acc[g][r], -S));
+        if (ln < TILE_TOKENS) {
+            ssr[wave][ln] = ss;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zred[wave][ln][4 * g + r] = zsum[g][r];
+        }
         __syncthreads();
         if (tid_l < TILE_TOKENS * M) {
             const int tt = tid_l / M, row = tid_l % M;
+            float sst = ssr[0][tt];
+#pragma unroll
+            for (int w = 1; w < TILE_WAVES; ++w) sst += ssr[w][tt];
+            const float inv_r = 1.0f / sqrtf(sst / (float)K + eps);
             float s = zred[0][tt][row];
 #pragma unroll
             for (int w = 1; w < TILE_WAVES; ++w) s += zred[w][tt][row];
-            const float z = s + bias[row];
+            const float z = s * inv_r + bias_row;
             zs[tt][row] = z;
             const size_t tk = tile0 + tt;
             if (logits && tk < (size_t)T) logits[tk * M + row] = z;
