@@ -119,6 +119,137 @@ def copy_calibration(nbytes=1 << 30):
           flush=True)
 
 
+def sweep_paths(Ts=(1, 2, 3, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096), steps=200, warmup=20):
+    """Per-call time of each kernel path of ds4hc_fused across T (the split-K / tile
+    crossover), warm: the same inputs every call, as in a decode or verify loop."""
+    import torch
+    from deepseek_v4_hyper_amd import binding as B
+    from deepseek_v4_hyper_amd import workloads as wl
+    paths = {"splitk": B.DS4HC_FLAG_FORCE_SPLITK, "tile": B.DS4HC_FLAG_FORCE_TILE,
+             "rowres": B.DS4HC_FLAG_FORCE_ROWRES, "default": 0}
+    for T in Ts:
+        c = wl.make_verify(0, T=T)
+        X, W, b, lo = to_device(c)
+        li = torch.empty((T, c.d), dtype=X.dtype, device="cuda")
+        m = 2 * c.n + c.n * c.n
+        cf = torch.empty((T, m), dtype=torch.float32, device="cuda")
+        xo = torch.empty_like(X)
+        stream = torch.cuda.current_stream()
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        for name, fl in paths.items():
+            params = B.make_params(c.n, c.d, c.eps, c.iters, fl)
+            wsb = B.ds4hc_workspace_bytes(params, T, B.DS4HC_F32)
+            ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+            ptr = [ctypes.c_void_p(t.data_ptr()) for t in (X, W, b, lo, li, cf, xo, ws)]
+
+            def call():
+                st = B.ds4hc_fused_raw(params, T, B.DS4HC_F32, *ptr[:7], ptr[7], wsb, sp)
+                if st != B.DS4HC_OK:
+                    raise B.Ds4hcError(st, "ds4hc_fused")
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            print(json.dumps({"sweep": "ds4hc_fused", "T": T, "n_hc": c.n, "d": c.d, "dtype": "f32",
+                              "path": name, "us_per_call": us, "tokens_per_s": T / (us * 1e-6)}),
+                  flush=True)
+
+
+def decode_chain(sites=86, d=4096, n=4, reps=20):
+    """Decode-token chain of `sites` HC sites (attention and FFN per layer, 43 layers),
+    T = 1, each site with its own f16 weight; the layer body is the stand-in
+    layer_out = 0.5 * layer_in + noise (one elementwise kernel). Variants: two
+    library calls per site (ds4hc_pre ... ds4hc_post) or one (ds4hc_post_pre at
+    every boundary); each run eagerly and as one captured HIP graph. Prints one
+    JSON line per variant: microseconds per site and per token."""
+    import torch
+    from deepseek_v4_hyper_amd import binding as B
+    from deepseek_v4_hyper_amd import workloads as wl
+    m = 2 * n + n * n
+    rng = np.random.Generator(np.random.PCG64(0))
+    X0 = torch.from_numpy(rng.standard_normal((1, n, d), dtype=np.float32)).cuda()
+    Ws = [torch.from_numpy((rng.standard_normal((m, n * d), dtype=np.float32) * 0.02)
+                           .astype(np.float16)).cuda() for _ in range(sites)]
+    noise = torch.from_numpy(rng.standard_normal((sites, 1, d), dtype=np.float32) * 0.1).cuda()
+    bias = torch.zeros(m, dtype=torch.float32, device="cuda")
+    Xa, Xb = torch.empty_like(X0), torch.empty_like(X0)
+    li = torch.empty((1, d), device="cuda")
+    lo = torch.empty((1, d), device="cuda")
+    cf = [torch.empty((1, m), device="cuda") for _ in range(2)]
+    p = B.make_params(n, d)
+    wsb = max(B.ds4hc_workspace_bytes(p, 1, B.DS4HC_F32), B.ds4hc_post_pre_workspace_bytes(p, 1, B.DS4HC_F32))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    P = ctypes.c_void_p
+    pt = lambda t: P(t.data_ptr())
+
+    def chk(st, what):
+        if st != B.DS4HC_OK:
+            raise B.Ds4hcError(st, what)
+
+    def run(one_pass):
+        sp = P(torch.cuda.current_stream().cuda_stream)
+        Xa.copy_(X0)
+        cur, nxt = Xa, Xb
+        chk(B.ds4hc_pre_raw(p, 1, 0, pt(cur), pt(Ws[0]), pt(bias), pt(li), pt(cf[0]), None, pt(ws),
+                            wsb, sp), "pre")
+        for s_ in range(sites):
+            torch.add(noise[s_], li, alpha=0.5, out=lo)
+            c_now, c_next = cf[s_ % 2], cf[(s_ + 1) % 2]
+            if s_ + 1 < sites and one_pass:
+                chk(B.ds4hc_post_pre_raw(p, 1, 0, pt(cur), pt(c_now), pt(lo), pt(Ws[s_ + 1]), pt(bias),
+                                         pt(nxt), pt(li), pt(c_next), None, pt(ws), wsb, sp), "post_pre")
+            else:
+                chk(B.ds4hc_post_raw(p, 1, 0, pt(cur), pt(c_now), pt(lo), pt(nxt), sp), "post")
+                if s_ + 1 < sites:
+                    chk(B.ds4hc_pre_raw(p, 1, 0, pt(nxt), pt(Ws[s_ + 1]), pt(bias), pt(li), pt(c_next),
+                                        None, pt(ws), wsb, sp), "pre")
+            cur, nxt = nxt, cur
+        return cur
+
+    results = {}
+    for one_pass in (False, True):
+        for _ in range(3):
+            out = run(one_pass)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run(one_pass)
+        e1.record()
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / reps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gout = run(one_pass)
+        # replays, each checked against the eager result with eager work in between
+        for _ in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(gout, ref):
+                raise RuntimeError("graph replay differs from the eager chain")
+            run(one_pass)
+            torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / reps
+        name = "post_pre" if one_pass else "pre+post"
+        results[name] = (eager_us, graph_us)
+        for mode, us in (("eager", eager_us), ("graph", graph_us)):
+            print(json.dumps({"chain": "decode", "sites": sites, "T": 1, "n_hc": n, "d": d, "dtype": "f32",
+                              "calls_per_site": 1 if one_pass else 2, "variant": name, "mode": mode,
+                              "us_per_token": us, "us_per_site": us / sites}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +262,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--chain", action="store_true",
+                    help="instead of the benchmark line: the 86-site decode chain (T=1, n=4, d=4096, "
+                         "fp32), eager and HIP-graph replay, two calls per site vs one-pass post+pre")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line: time every kernel path of ds4hc_fused over "
+                         "T = 1..4096 (verify recipe, n=4, d=4096, fp32), one JSON line per (T, path)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -143,6 +280,12 @@ def main():
     from deepseek_v4_hyper_amd import workloads as wl
 
     B.load()
+    if args.sweep:
+        sweep_paths()
+        return
+    if args.chain:
+        decode_chain()
+        return
     cases = [make_case(args.workload, s) for s in range(args.sets)]
     c0 = cases[0]
     T, n, d = c0.T, c0.n, c0.d

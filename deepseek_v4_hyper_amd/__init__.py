@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     Ds4hcError,
     ds4hc_fused,
     ds4hc_post,
+    ds4hc_post_pre,
+    ds4hc_post_pre_workspace_bytes,
     ds4hc_pre,
     ds4hc_sinkhorn,
     ds4hc_workspace_bytes,

@@ -26,6 +26,7 @@ DS4HC_FLAG_FORCE_SPLITK = 4
 DS4HC_FLAG_FORCE_TILE = 8
 
 EXPORTED = ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused", "ds4hc_workspace_bytes",
+            "ds4hc_post_pre", "ds4hc_post_pre_workspace_bytes",
             "ds4hc_status_string", "ds4hc_last_hip_error", "ds4hc_abi_version")
 
 
@@ -66,10 +67,12 @@ def load(path: str = LIB_PATH):
     lib.ds4hc_sinkhorn.argtypes = [i64, i32, i32, vp, vp, vp]
     lib.ds4hc_post.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp]
     lib.ds4hc_fused.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused"):
+    lib.ds4hc_post_pre.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused", "ds4hc_post_pre"):
         getattr(lib, f).restype = ctypes.c_int
-    lib.ds4hc_workspace_bytes.argtypes = [P, i64, ctypes.c_int]
-    lib.ds4hc_workspace_bytes.restype = sz
+    for f in ("ds4hc_workspace_bytes", "ds4hc_post_pre_workspace_bytes"):
+        getattr(lib, f).argtypes = [P, i64, ctypes.c_int]
+        getattr(lib, f).restype = sz
     lib.ds4hc_status_string.argtypes = [ctypes.c_int]
     lib.ds4hc_status_string.restype = ctypes.c_char_p
     lib.ds4hc_last_hip_error.restype = ctypes.c_char_p
@@ -99,6 +102,17 @@ def _check(status: int, where: str):
 
 def ds4hc_workspace_bytes(params: Params, T: int, dtype: int) -> int:
     return int(load().ds4hc_workspace_bytes(ctypes.byref(params), int(T), int(dtype)))
+
+
+def ds4hc_post_pre_workspace_bytes(params: Params, T: int, dtype: int) -> int:
+    return int(load().ds4hc_post_pre_workspace_bytes(ctypes.byref(params), int(T), int(dtype)))
+
+
+def ds4hc_post_pre_raw(params, T, dtype, X, coeffs_prev, layer_out, W_next, bias_next, X_out,
+                       layer_in, coeffs, logits, ws, ws_bytes, stream):
+    return load().ds4hc_post_pre(ctypes.byref(params), int(T), int(dtype), X, coeffs_prev,
+                                 layer_out, W_next, bias_next, X_out, layer_in, coeffs, logits, ws,
+                                 int(ws_bytes), stream)
 
 
 def ds4hc_pre_raw(params, T, dtype, X, W, bias, layer_in, coeffs, logits, ws, ws_bytes, stream):
@@ -230,6 +244,41 @@ def ds4hc_post(X, coeffs, layer_out, *, X_out=None, stream=None, rms_eps=1e-6,
     _check(ds4hc_post_raw(p, T, dt, _ptr(X), _ptr(coeffs), _ptr(layer_out), _ptr(X_out),
                           _stream(stream)), "ds4hc_post")
     return X_out
+
+
+def ds4hc_post_pre(X, coeffs_prev, layer_out, W_next, bias_next, *, rms_eps=1e-6,
+                   sinkhorn_iters=20, flags=0, X_out=None, layer_in=None, coeffs=None,
+                   logits=None, workspace=None, stream=None, want_logits=False):
+    """post(l) then pre(l+1): X' = H_l.X + post_l (x) layer_out_l, then HC-pre of
+    site l+1 on X'. Returns (X_out [T,n,d], layer_in [T,d], coeffs [T,m], logits or None).
+    X_out may be X itself (in place)."""
+    torch = _torch()
+    T, n, d = X.shape
+    m = 2 * n + n * n
+    dt = _state_code(X)
+    p = make_params(n, d, rms_eps, sinkhorn_iters, flags)
+    _need(X, (T, n, d), X.dtype, "X")
+    _need(coeffs_prev, (T, m), torch.float32, "coeffs_prev")
+    _need(layer_out, (T, d), X.dtype, "layer_out")
+    _need(W_next, (m, n * d), torch.float16, "W_next")
+    _need(bias_next, (m,), torch.float32, "bias_next")
+    if X_out is None:
+        X_out = torch.empty_like(X)
+    if layer_in is None:
+        layer_in = torch.empty((T, d), dtype=X.dtype, device=X.device)
+    if coeffs is None:
+        coeffs = torch.empty((T, m), dtype=torch.float32, device=X.device)
+    if logits is None and want_logits:
+        logits = torch.empty((T, m), dtype=torch.float32, device=X.device)
+    need = ds4hc_post_pre_workspace_bytes(p, T, dt)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(ds4hc_post_pre_raw(p, T, dt, _ptr(X), _ptr(coeffs_prev), _ptr(layer_out), _ptr(W_next),
+                              _ptr(bias_next), _ptr(X_out), _ptr(layer_in), _ptr(coeffs),
+                              _ptr(logits), _ptr(workspace), ws_bytes, _stream(stream)),
+           "ds4hc_post_pre")
+    return X_out, layer_in, coeffs, logits
 
 
 def ds4hc_sinkhorn(logits_res, *, iters=20, H=None, stream=None):

@@ -17,7 +17,12 @@
 
 namespace {
 
-constexpr int64_t SPLITK_MAX_T = 32;       // T at or below which split-K is the default
+// Default paths by T, from a sweep of every path of ds4hc_fused on MI355X at
+// n = 4, d = 4096, fp32 (bench.py --sweep): split-K is fastest through T = 128
+// (21 us against 35 us for the tile kernel), the row-resident kernel at
+// T = 256 (30 us against 34 and 36), the tile kernel from T = 512 on.
+constexpr int64_t SPLITK_MAX_T = 160;      // T at or below which split-K is the default
+constexpr int64_t ROWRES_MAX_T = 384;      // then the row-resident kernel up to here
 constexpr int64_t MAX_T = int64_t(1) << 24;
 constexpr int MAX_ITERS = 1000;
 constexpr uint64_t MAX_WORK_ITEMS = 0xFFFFFFFFull;  // HSA dispatch grid size is 32-bit
@@ -71,11 +76,11 @@ struct Plan {
 };
 
 // Path for HC-pre / fused: split-K for small T (the fn weight dominates the
-// bytes and must be spread over many CUs), the persistent MFMA tile kernel
-// for large T (measured on MI355X at n = 4: 184 us against 280 us for the
-// one-token VALU kernel at T = 4096, d = 4096 float32, and 691 us against
-// 1333 us at T = 16384, d = 7168 bfloat16), then the VALU kernel, then
-// split-K where a row is too long for either.
+// bytes and must be spread over many CUs), the one-token VALU kernel for
+// middling T, the persistent MFMA tile kernel for large T (measured on MI355X
+// at n = 4: 178 us against 280 us for the VALU kernel at T = 4096, d = 4096
+// float32, and 703 us against 1333 us at T = 16384, d = 7168 bfloat16), then
+// the VALU kernel, then split-K where a row is too long for either.
 // Returns UNSUPPORTED if a forced path cannot take the shape or a launch
 // would not fit.
 ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *out) {
@@ -95,7 +100,9 @@ ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *o
     } else if (T <= SPLITK_MAX_T) {
         path = ds4hc::PATH_SPLITK;
     } else {
-        path = fits_tile ? ds4hc::PATH_TILE : fits_rowres ? ds4hc::PATH_ROWRES : ds4hc::PATH_SPLITK;
+        const bool mid = T <= ROWRES_MAX_T && fits_rowres;
+        path = mid ? ds4hc::PATH_ROWRES
+                   : fits_tile ? ds4hc::PATH_TILE : fits_rowres ? ds4hc::PATH_ROWRES : ds4hc::PATH_SPLITK;
     }
     Plan pl{path, 0, 0};
     if (path == ds4hc::PATH_ROWRES) {
@@ -161,9 +168,89 @@ ds4hc_status run_hc(bool fused, const ds4hc_params *p, int64_t T, ds4hc_dtype dt
     return e == hipSuccess ? DS4HC_OK : hip_fail(e);
 }
 
+// Plan for post(l) + pre(l+1): one pass over the state for small T (split-K
+// over column chunks; also when split-K is forced), else post then the pre
+// path make_plan picks (or the forced one).
+struct PostPrePlan {
+    bool one_pass;
+    Plan pre;          // pre path when !one_pass
+    uint64_t ws_bytes;
+};
+
+ds4hc_status make_post_pre_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, PostPrePlan *out) {
+    const uint32_t force = p->flags & FORCE_FLAGS;
+    PostPrePlan pp{};
+    pp.one_pass = force == DS4HC_FLAG_FORCE_SPLITK || (force == 0 && T <= SPLITK_MAX_T);
+    if (pp.one_pass) {
+        const int m = 2 * p->n_hc + p->n_hc * p->n_hc;
+        const uint64_t P2 = (uint64_t)ds4hc::post_pre_chunks(p->d, dt);
+        const uint64_t tg = (uint64_t)(T + 3) / 4;
+        if (tg * 64u > MAX_WORK_ITEMS || P2 > 0xFFFFu || (uint64_t)T * 64u > MAX_WORK_ITEMS)
+            return DS4HC_ERR_UNSUPPORTED;
+        pp.ws_bytes = P2 * (uint64_t)T * (uint64_t)(m + 1) * sizeof(float);
+    } else {
+        const ds4hc_status st = make_plan(p, T, dt, &pp.pre);
+        if (st != DS4HC_OK) return st;
+        const uint64_t cb = (uint64_t)(p->d + 64 * vec_elems(dt) - 1) / (64 * vec_elems(dt));
+        if (cb > 0xFFFFu || (uint64_t)T * 64u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
+        pp.ws_bytes = pp.pre.ws_bytes;
+    }
+    *out = pp;
+    return DS4HC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+ds4hc_status ds4hc_post_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                            const float *coeffs_prev, const void *layer_out,
+                            const uint16_t *W_f16_next, const float *bias_next, void *X_out,
+                            void *layer_in, float *coeffs, float *logits_opt, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    ds4hc_status st = check_params(p, T, dtype);
+    if (st != DS4HC_OK || T == 0) return st;
+    if (!X || !coeffs_prev || !layer_out || !W_f16_next || !bias_next || !X_out || !layer_in ||
+        !coeffs)
+        return DS4HC_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(layer_out, 16) || !aligned(W_f16_next, 16) ||
+        !aligned(X_out, 16) || !aligned(layer_in, 16) || !aligned(coeffs_prev, 4) ||
+        !aligned(bias_next, 4) || !aligned(coeffs, 4) || (logits_opt && !aligned(logits_opt, 4)) ||
+        (workspace && !aligned(workspace, 4)))
+        return DS4HC_ERR_INVALID_ARG;
+    PostPrePlan pp;
+    st = make_post_pre_plan(p, T, dtype, &pp);
+    if (st != DS4HC_OK) return st;
+    if (pp.ws_bytes > 0 && (!workspace || workspace_bytes < pp.ws_bytes)) return DS4HC_ERR_INVALID_ARG;
+
+    const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
+    const uint64_t sb = (uint64_t)state_bytes(dtype), K = (uint64_t)n * d, uT = (uint64_t)T;
+    const Range rX{X, uT * K * sb}, rcp{coeffs_prev, uT * m * 4}, rlo{layer_out, uT * d * sb};
+    const Range rW{W_f16_next, (uint64_t)m * K * 2}, rb{bias_next, (uint64_t)m * 4};
+    const Range rXo{X_out, uT * K * sb}, rli{layer_in, uT * d * sb}, rc{coeffs, uT * m * 4};
+    const Range rz{logits_opt, uT * m * 4}, rws{pp.ws_bytes ? workspace : nullptr, pp.ws_bytes};
+    // Outputs must not overlap any other buffer, except that X_out may be exactly X.
+    const Range all[] = {rX, rcp, rlo, rW, rb, rXo, rli, rc, rz, rws};
+    constexpr int FIRST_OUT = 5, N_ALL = 10;
+    for (int a = FIRST_OUT; a < N_ALL; ++a) {
+        for (int b = 0; b < N_ALL; ++b) {
+            if (a == b) continue;
+            const bool in_place = ((a == 5 && b == 0) || (a == 0 && b == 5)) && X_out == X;
+            if (!in_place && overlap(all[a], all[b])) return DS4HC_ERR_INVALID_ARG;
+        }
+    }
+    ds4hc::FusedArgs a{n, d, (int)dtype, p->sinkhorn_iters, T, p->rms_eps, X, W_f16_next, bias_next,
+                       layer_out, layer_in, coeffs, logits_opt, X_out, static_cast<float *>(workspace)};
+    const hipError_t e = ds4hc::launch_post_pre(a, coeffs_prev, pp.one_pass, pp.pre.path, stream);
+    return e == hipSuccess ? DS4HC_OK : hip_fail(e);
+}
+
+size_t ds4hc_post_pre_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype) {
+    if (check_params(p, T, dtype) != DS4HC_OK) return 0;
+    PostPrePlan pp;
+    if (make_post_pre_plan(p, T, dtype, &pp) != DS4HC_OK) return 0;
+    return (size_t)pp.ws_bytes;
+}
 
 ds4hc_status ds4hc_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
                        const uint16_t *W_f16, const float *bias, void *layer_in, float *coeffs,

@@ -117,13 +117,25 @@ __device__ __forceinline__ float half_get(const HalfVec<V> &h, int e) {
     return (e & 1) ? f16_hi(w) : f16_lo(w);
 }
 
-// Sum over the 64 lanes of a wavefront by xor butterfly. Every lane ends with
-// the same bits: each step adds two identical pairs in commutative order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront, entirely in the VALU: quad butterflies
+// (lane ^ 1, lane ^ 2), then the quads of a 16-lane row (rotations by 8, then
+// 4), then the gfx950 row swaps (rows 0<->1 and 2<->3, then the halves). Each
+// step adds the same two partial sums in every lane that receives them, so
+// every lane ends with the same bits.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1)
-        v += __shfl_xor(v, s, 64);
-    return v;
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x128>(v);  // row_ror:8
+    v += dpp_mov<0x124>(v);  // row_ror:4
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Register-resident Sinkhorn. Lanes form groups of N*N; lane l of a group
@@ -150,12 +162,6 @@ __device__ __forceinline__ float sinkhorn_lane(float z, int iters) {
         m = m / cs;
     }
     return m;
-}
-
-// DPP lane exchange of a float (quad permutes and row rotations).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
 // Same result as sinkhorn_lane, with the lane exchanges done by DPP (no LDS

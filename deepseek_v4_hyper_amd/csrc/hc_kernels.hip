@@ -140,7 +140,7 @@ __global__ __launch_bounds__(ROWRES_THREADS) void hc_rowres_kernel(
         // Residual logits z_{2N + l} moved to lane l of every N*N group.
         const int src = 2 * N + (lane % (N * N));
         const float zr = __shfl(z, src, 64);
-        const float h = sinkhorn_lane<N>(zr, iters);
+        const float h = sinkhorn_lane_dpp<N>(zr, iters);
         if (lane < N * N) {
             cf[2 * N + lane] = h;
             if (coeffs) coeffs[t * M + 2 * N + lane] = h;
@@ -789,6 +789,90 @@ __global__ __launch_bounds__(64) void hc_partials_kernel(int d, int T, const voi
 }
 
 // ---------------------------------------------------------------------------
+// One-pass chain step, split-K part: grid (ceil(T / SPLITK_TOKENS), P2), one
+// wavefront. Chunk p covers columns [p*64*V, (p+1)*64*V) of every stream, so a
+// lane holds all n streams of its V columns and can apply the previous site's
+// post update X' = H.X + post (x) layer_out itself (same operation order as
+// hc_post_kernel, so X' is bitwise what ds4hc_post writes). It stores X' and
+// writes the partial dots of the next site's fn projection and the partial
+// sum of squares of X' (as rounded to the state type) to ws[p][t][0..M].
+// ---------------------------------------------------------------------------
+template <int N, int DT>
+__global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
+    int d, int T, const void *__restrict__ X, const float *__restrict__ coeffs_prev,
+    const void *__restrict__ layer_out, const uint16_t *__restrict__ W, void *X_out,
+    float *__restrict__ ws) {
+    constexpr int V = StateVec<DT>::V;
+    constexpr int M = n_logits(N);
+    const int lane = threadIdx.x;
+    const size_t K = (size_t)N * d;
+    const int c0 = (blockIdx.y * 64 + lane) * V;
+    const bool ok = c0 < d;
+    const int tbase = blockIdx.x * SPLITK_TOKENS;
+
+#pragma unroll
+    for (int tt = 0; tt < SPLITK_TOKENS; ++tt) {
+        const int t = tbase + tt;
+        if (t >= T) break;  // uniform across the wavefront
+        const float *cp = coeffs_prev + (size_t)t * M;
+        float x[N][V];
+        float acc[M + 1];
+#pragma unroll
+        for (int j = 0; j <= M; ++j) acc[j] = 0.f;
+        if (ok) {
+            float xin[N][V];
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const StateVec<DT> v = load_vec<DT>(X, (size_t)t * K + (size_t)i * d + c0);
+#pragma unroll
+                for (int e = 0; e < V; ++e) xin[i][e] = vec_get<DT>(v, e);
+            }
+            const StateVec<DT> lv = load_vec<DT>(layer_out, (size_t)t * d + c0);
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    float s = cp[2 * N + i * N] * xin[0][e];
+#pragma unroll
+                    for (int j = 1; j < N; ++j) s = fmaf(cp[2 * N + i * N + j], xin[j][e], s);
+                    o[e] = fmaf(cp[N + i], vec_get<DT>(lv, e), s);
+                }
+                store_vec<DT>(X_out, (size_t)t * K + (size_t)i * d + c0, o);
+                // the next site sees X' as stored (rounded to the state type)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    if constexpr (DT == DT_F32)
+                        x[i][e] = o[e];
+                    else
+                        x[i][e] = bf16_lo(f32_to_bf16_bits(o[e]));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+#pragma unroll
+                for (int j = 0; j < M; ++j) {
+                    const HalfVec<V> w = load_half_vec<V>(W + (size_t)j * K + (size_t)i * d + c0);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) acc[j] = fmaf(half_get<V>(w, e), x[i][e], acc[j]);
+                }
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[M] = fmaf(x[i][e], x[i][e], acc[M]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j <= M; ++j) acc[j] = wave_sum(acc[j]);
+        if (lane <= M) {
+            float v = acc[0];
+#pragma unroll
+            for (int j = 1; j <= M; ++j)
+                if (lane == j) v = acc[j];
+            ws[((size_t)blockIdx.y * T + t) * (M + 1) + lane] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Split-K finish: grid (T, ceil(d / (64*V))), one wavefront. Combines the P
 // partials of token t in chunk order, computes logits, gates and Sinkhorn,
 // then the pre-mix (and post update) of 64*V columns.
@@ -809,7 +893,16 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
     if (lane <= M) {
         const float *p = ws + t * (M + 1) + lane;
         const size_t stride = (size_t)T * (M + 1);
-        for (int c = 0; c < P; ++c) tot += p[(size_t)c * stride];
+        // chunk order, eight loads in flight at a time
+        int c = 0;
+        for (; c + 8 <= P; c += 8) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = p[(size_t)(c + k) * stride];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) tot += v[k];
+        }
+        for (; c < P; ++c) tot += p[(size_t)c * stride];
     }
     const float ssum = __shfl(tot, M, 64);
     const float r = sqrtf(ssum / (float)K + eps);
@@ -823,7 +916,7 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
     }
     if (writer && logits && lane < M) logits[t * M + lane] = z;
     const float zr = __shfl(z, 2 * N + (lane % (N * N)), 64);
-    const float h = sinkhorn_lane<N>(zr, iters);
+    const float h = sinkhorn_lane_dpp<N>(zr, iters);
     if (lane < N * N) {
         cf[2 * N + lane] = h;
         if (writer && coeffs) coeffs[t * M + 2 * N + lane] = h;
@@ -917,7 +1010,7 @@ __global__ __launch_bounds__(64) void hc_sinkhorn_kernel(int T, int iters,
     const int e = lane % NN;
     const bool ok = t < (size_t)T;
     const float z = ok ? Z[t * NN + e] : 0.f;
-    const float h = sinkhorn_lane<N>(z, iters);
+    const float h = sinkhorn_lane_dpp<N>(z, iters);
     if (ok) H[t * NN + e] = h;
 }
 
@@ -1063,6 +1156,49 @@ hipError_t launch_hc(const FusedArgs &a, bool fused, int path, hipStream_t s) {
     case 4: return dispatch_dt<4>(a.dt, fused, path, a, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <int N, int DT>
+static hipError_t launch_post_pre_n(const FusedArgs &a, const float *coeffs_prev, hipStream_t s) {
+    constexpr int V = StateVec<DT>::V;
+    const int P2 = (a.d + 64 * V - 1) / (64 * V);
+    const dim3 g1((unsigned)((a.T + SPLITK_TOKENS - 1) / SPLITK_TOKENS), (unsigned)P2);
+    hipError_t e = launch_kernel(hc_postpre_partials_kernel<N, DT>, g1, dim3(64), s, a.d, (int)a.T,
+                                 a.X, coeffs_prev, a.layer_out, a.W, a.X_out, a.ws);
+    if (e != hipSuccess) return e;
+    // the pre-mix reads X' back from X_out; no post update here
+    const dim3 g2((unsigned)a.T, (unsigned)P2);
+    return launch_kernel(hc_finish_kernel<N, DT, MODE_PRE>, g2, dim3(64), s, a.d, (int)a.T, P2,
+                         a.eps, a.iters, (const void *)a.X_out, a.bias, (const float *)a.ws,
+                         (const void *)nullptr, a.layer_in, a.coeffs, a.logits, (void *)nullptr);
+}
+
+int post_pre_chunks(int d, int dt) {
+    const int V = dt == DT_F32 ? 4 : 8;
+    return (d + 64 * V - 1) / (64 * V);
+}
+
+hipError_t launch_post_pre(const FusedArgs &a, const float *coeffs_prev, bool one_pass, int path,
+                           hipStream_t s) {
+    if (!one_pass) {
+        // post then pre on X' (two passes over the state)
+        hipError_t e = launch_post(a.n, a.dt, a.d, a.T, a.X, coeffs_prev, a.layer_out, a.X_out, s);
+        if (e != hipSuccess) return e;
+        FusedArgs b = a;
+        b.X = a.X_out;
+        b.layer_out = nullptr;
+        return launch_hc(b, false, path, s);
+    }
+#define DS4HC_PP(NN)                                                                             \
+    return a.dt == DT_F32 ? launch_post_pre_n<NN, DT_F32>(a, coeffs_prev, s)                     \
+                          : launch_post_pre_n<NN, DT_BF16>(a, coeffs_prev, s)
+    switch (a.n) {
+    case 1: DS4HC_PP(1);
+    case 2: DS4HC_PP(2);
+    case 4: DS4HC_PP(4);
+    }
+#undef DS4HC_PP
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_post(int n, int dt, int d, int64_t T, const void *X, const float *coeffs,

@@ -38,6 +38,12 @@ hipError_t launch_hc(const FusedArgs &a, bool fused, int path, hipStream_t s);
 hipError_t launch_post(int n, int dt, int d, int64_t T, const void *X, const float *coeffs,
                        const void *layer_out, void *X_out, hipStream_t s);
 hipError_t launch_sinkhorn(int n, int iters, int64_t T, const float *Z, float *H, hipStream_t s);
+// post(l) + pre(l+1): one pass (split-K chunks over columns, then the combining
+// kernel) or post then pre on `path`. a.X = X_l, a.layer_out = layer_out_l,
+// a.X_out = X_{l+1}, a.W/bias/layer_in/coeffs/logits = site l+1.
+int post_pre_chunks(int d, int dt);
+hipError_t launch_post_pre(const FusedArgs &a, const float *coeffs_prev, bool one_pass, int path,
+                           hipStream_t s);
 
 // hipLaunchKernel with the kernel's own parameter types, so the launch status
 // comes back directly instead of through the thread's sticky last-error slot.

@@ -151,6 +151,39 @@ ds4hc_status ds4hc_fused(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, co
  * the chosen path needs none). Pure function; 0 for invalid arguments. */
 size_t ds4hc_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype);
 
+/*
+ * ds4hc_post_pre -- one decode-chain step: the post update of site l followed
+ * by HC-pre of site l+1, the two halves the pages run back to back on the GPU
+ * with no host round trip between them ("hc_post" and "HC-pre", lucebox-hub
+ * PR #494, comment on the GPU HC pre-mix and hc_post). With
+ *   X' = H_l . X + post_l (x) layer_out_l            (coefficients from site l)
+ * it writes X_out = X' and, for site l+1 on X' (as stored, in the state dtype):
+ * layer_in = pre-mix, coeffs = pre | post | H, logits_opt = raw z.
+ *   X            [T, n, d]  state dtype  (read)  state before site l's post
+ *   coeffs_prev  [T, m]     float32      (read)  site l's coefficients
+ *   layer_out    [T, d]     state dtype  (read)  site l's layer output
+ *   W_f16_next   [m, n*d]   float16 bits (read)  site l+1's fn weight
+ *   bias_next    [m]        float32      (read)
+ *   X_out        [T, n, d]  state dtype  (written; may be exactly X)
+ *   layer_in     [T, d]     state dtype  (written)
+ *   coeffs       [T, m]     float32      (written; must not overlap coeffs_prev)
+ *   workspace    >= ds4hc_post_pre_workspace_bytes(p, T, dtype) bytes
+ * X' is bitwise what ds4hc_post writes. For T <= 160 (or DS4HC_FLAG_FORCE_SPLITK)
+ * the state is read once: a split-K kernel over column chunks applies the post
+ * update, stores X' and accumulates site l+1's partial projections, then a
+ * combining kernel finishes site l+1. Otherwise it runs the post kernel, then
+ * HC-pre on the path ds4hc_pre would take (or the forced one). Errors as for
+ * ds4hc_fused.
+ */
+ds4hc_status ds4hc_post_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                            const float *coeffs_prev, const void *layer_out,
+                            const uint16_t *W_f16_next, const float *bias_next, void *X_out,
+                            void *layer_in, float *coeffs, float *logits_opt, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes ds4hc_post_pre needs for these arguments (0 if none or invalid). */
+size_t ds4hc_post_pre_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype);
+
 /* Static, human-readable name of a status code. */
 const char *ds4hc_status_string(ds4hc_status s);
 

@@ -68,13 +68,12 @@ def test_version_and_status_strings():
 
 def test_workspace_bytes_is_pure_and_path_dependent():
     p = B.make_params(4, 4096)
-    # decode-sized T takes the split-K path: chunks * T * (m + 1) floats
+    # T up to 160 takes the split-K path: chunks * T * (m + 1) floats
     P = (4 * 4096) // 256
     assert B.ds4hc_workspace_bytes(p, 1, B.DS4HC_F32) == P * 1 * 25 * 4
     assert B.ds4hc_workspace_bytes(p, 4, B.DS4HC_F32) == P * 4 * 25 * 4
     Pb = (4 * 4096) // 512
     assert B.ds4hc_workspace_bytes(p, 4, B.DS4HC_BF16) == Pb * 4 * 25 * 4
-    # large T: the row-resident kernel needs no workspace
     assert B.ds4hc_workspace_bytes(p, 4096, B.DS4HC_F32) == 0
     pf = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_SPLITK)
     assert B.ds4hc_workspace_bytes(pf, 4096, B.DS4HC_F32) == P * 4096 * 25 * 4
@@ -158,7 +157,7 @@ def test_fused_rejects_small_workspace():
 @no_gpu_only
 def test_fused_rejects_overlaps_but_allows_in_place():
     p = B.make_params(4, 4096)
-    T = 64  # row-resident path: no workspace
+    T = 4096  # tile path: no workspace
     # layer_in inside X
     assert fused(p, T, layer_in=fake(0, 4096)) == B.DS4HC_ERR_INVALID_ARG
     # X_out overlapping X by a shifted window
@@ -195,3 +194,59 @@ def test_pre_post_sinkhorn_validation():
     assert B.ds4hc_pre_raw(p, 0, 0, None, None, None, None, None, None, None, 0,
                            None) == B.DS4HC_OK
     assert fused(p, 0, X=None, W=None, layer_in=None, ws=None) == B.DS4HC_OK
+
+
+def post_pre(p, T=8, dt=B.DS4HC_F32, **over):
+    args = dict(X=fake(0), cp=fake(1), lo=fake(2), W=fake(3), b=fake(4), X_out=fake(5),
+                li=fake(6), c=fake(7), z=None, ws=fake(8), ws_bytes=1 << 30)
+    args.update(over)
+    return B.ds4hc_post_pre_raw(p, T, dt, args["X"], args["cp"], args["lo"], args["W"], args["b"],
+                                args["X_out"], args["li"], args["c"], args["z"], args["ws"],
+                                args["ws_bytes"], None)
+
+
+def test_post_pre_workspace_bytes():
+    p = B.make_params(4, 4096)
+    # one pass for T <= 32: column chunks of 64 lanes x V columns, (m + 1) floats per token
+    assert B.ds4hc_post_pre_workspace_bytes(p, 1, B.DS4HC_F32) == (4096 // 256) * 1 * 25 * 4
+    assert B.ds4hc_post_pre_workspace_bytes(p, 32, B.DS4HC_BF16) == (4096 // 512) * 32 * 25 * 4
+    assert B.ds4hc_post_pre_workspace_bytes(p, 160, B.DS4HC_F32) == 16 * 160 * 25 * 4
+    # larger T: post, then the pre path (row-resident or tile: none)
+    assert B.ds4hc_post_pre_workspace_bytes(p, 161, B.DS4HC_F32) == 0
+    assert B.ds4hc_post_pre_workspace_bytes(p, 4096, B.DS4HC_F32) == 0
+    pf = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_SPLITK)
+    assert B.ds4hc_post_pre_workspace_bytes(pf, 4096, B.DS4HC_F32) == 16 * 4096 * 25 * 4
+    assert B.ds4hc_post_pre_workspace_bytes(B.make_params(3, 4096), 1, B.DS4HC_F32) == 0
+
+
+@no_gpu_only
+@pytest.mark.parametrize("field", ["X", "cp", "lo", "W", "b", "X_out", "li", "c"])
+def test_post_pre_rejects_null_pointers(field):
+    assert post_pre(B.make_params(4, 4096), **{field: None}) == B.DS4HC_ERR_INVALID_ARG
+
+
+@no_gpu_only
+@pytest.mark.parametrize("field,idx,off", [("X", 0, 4), ("lo", 2, 8), ("W", 3, 2), ("X_out", 5, 4),
+                                           ("li", 6, 12), ("cp", 1, 2), ("c", 7, 1)])
+def test_post_pre_rejects_misaligned(field, idx, off):
+    assert post_pre(B.make_params(4, 4096), **{field: fake(idx, off)}) == B.DS4HC_ERR_INVALID_ARG
+
+
+@no_gpu_only
+def test_post_pre_overlaps_workspace_and_in_place():
+    p = B.make_params(4, 4096)
+    # new coefficients over the previous ones
+    assert post_pre(p, c=fake(1)) == B.DS4HC_ERR_INVALID_ARG
+    # X_out overlapping X by a shifted window; layer_in inside layer_out
+    assert post_pre(p, X_out=fake(0, 16)) == B.DS4HC_ERR_INVALID_ARG
+    assert post_pre(p, li=fake(2, 64)) == B.DS4HC_ERR_INVALID_ARG
+    # workspace too small or missing for the one-pass path
+    need = B.ds4hc_post_pre_workspace_bytes(p, 8, B.DS4HC_F32)
+    assert post_pre(p, ws_bytes=need - 4) == B.DS4HC_ERR_INVALID_ARG
+    assert post_pre(p, ws=None) == B.DS4HC_ERR_INVALID_ARG
+    # bad params; zero tokens ignore the pointers
+    assert post_pre(B.make_params(3, 4096)) == B.DS4HC_ERR_UNSUPPORTED
+    assert post_pre(p, 0, X=None, cp=None, lo=None, W=None, b=None, X_out=None, li=None, c=None,
+                    ws=None) == B.DS4HC_OK
+    # in place is allowed: validation passes, so without a GPU the launch fails (ERR_HIP)
+    assert post_pre(p, X_out=fake(0)) == B.DS4HC_ERR_HIP

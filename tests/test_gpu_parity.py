@@ -70,6 +70,15 @@ def test_verify_batch(path):
 
 
 @pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("q", [2, 3])
+def test_verify_widths(path, q):
+    """Speculative-verify batches of width q = 2 and 3 (adaptive draft widths):
+    a partly filled split-K token group and a partly filled tile."""
+    case = wl.make_verify(10 + q, T=q)
+    check_full(case, run_fused(case, FLAGS[path]), f"verify q={q}/{path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("T", [37, 67])
 def test_prefill_reduced_T(path, T):
     """Prefill shape and value recipe (per-token log-uniform scales) at a T the
@@ -339,3 +348,79 @@ def test_logits_output_matches_oracle():
         torch.cuda.synchronize()
         _, _, rz = oracle.pre(wl.state_to_f64(case.X, case.dtype), case.W, case.bias)
         assert_close_rows(z.cpu().numpy(), rz, 2e-5, "logits")
+
+
+# ------------------------------------------------------------------ one-pass chain step post(l) + pre(l+1)
+
+def _post_pre_case(seed, T, n, d, dtype):
+    """X, site l's coefficients (from ds4hc_pre with W_l), layer_out_l, and site l+1's weight."""
+    torch = torch_mod()
+    case = wl.make_random(seed, T, n, d, dtype)
+    nxt = wl.make_random(seed + 1000, 1, n, d, dtype)
+    X, W, b, lo = case_to_device(case)
+    _, c_prev, _ = B.ds4hc_pre(X, W, b)
+    Wn = torch.from_numpy(np.ascontiguousarray(nxt.W)).cuda()
+    bn = torch.from_numpy(np.ascontiguousarray(nxt.bias)).cuda()
+    return case, nxt, X, c_prev, lo, Wn, bn
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("n,d", [(4, 4096), (2, 264), (1, 1032), (4, 2056)])
+@pytest.mark.parametrize("T", [1, 3, 37])
+def test_post_pre_equals_post_then_pre(dtype, n, d, T):
+    """ds4hc_post_pre against ds4hc_post followed by ds4hc_pre (T = 1, 3: the one-pass
+    split-K kernels; T = 37: post then the tile path). X' must be bitwise what
+    ds4hc_post writes; layer_in and coeffs are checked against the oracle's HC-pre
+    of that X' and against the two-call path."""
+    torch = torch_mod()
+    case, nxt, X, c_prev, lo, Wn, bn = _post_pre_case(20 + T + n, T, n, d, dtype)
+    say(f"[gpu] ds4hc_post_pre T={T} n={n} d={d} {dtype}")
+    Xo, li, c, _ = B.ds4hc_post_pre(X, c_prev, lo, Wn, bn)
+    Xp = B.ds4hc_post(X, c_prev, lo)
+    li2, c2, _ = B.ds4hc_pre(Xp, Wn, bn)
+    torch.cuda.synchronize()
+    assert torch.equal(Xo, Xp)
+    tol = TOL[dtype]
+    rli, rc, _ = oracle.pre(torch_to_f64(Xo), nxt.W, nxt.bias)
+    assert_close_rows(torch_to_f64(li), rli, tol, "post_pre layer_in")
+    assert_coeffs(c.cpu().numpy().astype(np.float64), rc, "post_pre coeffs")
+    assert_close_rows(torch_to_f64(li), torch_to_f64(li2), tol, "post_pre vs two calls")
+    rxp = oracle.post(torch_to_f64(X), c_prev.cpu().numpy().astype(np.float64),
+                      torch_to_f64(lo))
+    assert_close_rows(torch_to_f64(Xo), rxp, tol, "post_pre X'")
+
+
+@pytest.mark.parametrize("T", [2, 40])
+def test_post_pre_in_place(T):
+    torch = torch_mod()
+    case, nxt, X, c_prev, lo, Wn, bn = _post_pre_case(31, T, 4, 4096, wl.F32)
+    say(f"[gpu] ds4hc_post_pre in place T={T}")
+    Xo, li, c, _ = B.ds4hc_post_pre(X, c_prev, lo, Wn, bn)
+    Xi = X.clone()
+    Xo2, li2, c2, _ = B.ds4hc_post_pre(Xi, c_prev, lo, Wn, bn, X_out=Xi)
+    torch.cuda.synchronize()
+    assert Xo2.data_ptr() == Xi.data_ptr()
+    assert torch.equal(Xi, Xo) and torch.equal(li2, li) and torch.equal(c2, c)
+
+
+def test_decode_chain_43_layers_post_pre():
+    """The 43-layer chain with one ds4hc_post_pre per layer boundary (ds4hc_pre for
+    the first site, ds4hc_post after the last): same end state as the oracle's chain."""
+    torch = torch_mod()
+    case = wl.make_chain(0)
+    X = state_to_torch(case.X, case.dtype)
+    b = torch.zeros(case.m, dtype=torch.float32, device="cuda")
+    Ws = [torch.from_numpy(w).cuda() for w in case.chain_W]
+    noise = torch.from_numpy(case.chain_noise).cuda()
+    say("[gpu] decode chain with ds4hc_post_pre: 43 layers, T=1, d=4096")
+    li, c, _ = B.ds4hc_pre(X, Ws[0], b)
+    for l in range(len(Ws)):
+        lo = li * 0.5 + noise[l][None, :]
+        if l + 1 < len(Ws):
+            X, li, c, _ = B.ds4hc_post_pre(X, c, lo, Ws[l + 1], b)
+        else:
+            X = B.ds4hc_post(X, c, lo)
+    torch.cuda.synchronize()
+    ref = oracle.chain(wl.state_to_f64(case.X, case.dtype), case.chain_W, case.bias, case.chain_noise)
+    e2e = assert_close_rows(torch_to_f64(X), ref[-1], 1e-4, "post_pre chain end to end")
+    say(f"    end-to-end {e2e:.2e}")
