@@ -12,7 +12,9 @@ from .binding import (  # noqa: F401
     DS4HC_FLAG_FORCE_SPLITK,
     DS4HC_FLAG_FORCE_TILE,
     Ds4hcError,
+    ds4hc_combine,
     ds4hc_fused,
+    ds4hc_partials,
     ds4hc_post,
     ds4hc_post_pre,
     ds4hc_post_pre_workspace_bytes,

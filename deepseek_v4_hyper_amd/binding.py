@@ -27,6 +27,7 @@ DS4HC_FLAG_FORCE_TILE = 8
 
 EXPORTED = ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused", "ds4hc_workspace_bytes",
             "ds4hc_post_pre", "ds4hc_post_pre_workspace_bytes",
+            "ds4hc_partials", "ds4hc_partials_workspace_bytes", "ds4hc_combine",
             "ds4hc_status_string", "ds4hc_last_hip_error", "ds4hc_abi_version")
 
 
@@ -68,9 +69,13 @@ def load(path: str = LIB_PATH):
     lib.ds4hc_post.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp]
     lib.ds4hc_fused.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ds4hc_post_pre.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused", "ds4hc_post_pre"):
+    lib.ds4hc_partials.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, sz, vp]
+    lib.ds4hc_combine.argtypes = [P, i32, i64, ctypes.c_int, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    for f in ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused", "ds4hc_post_pre",
+              "ds4hc_partials", "ds4hc_combine"):
         getattr(lib, f).restype = ctypes.c_int
-    for f in ("ds4hc_workspace_bytes", "ds4hc_post_pre_workspace_bytes"):
+    for f in ("ds4hc_workspace_bytes", "ds4hc_post_pre_workspace_bytes",
+              "ds4hc_partials_workspace_bytes"):
         getattr(lib, f).argtypes = [P, i64, ctypes.c_int]
         getattr(lib, f).restype = sz
     lib.ds4hc_status_string.argtypes = [ctypes.c_int]
@@ -279,6 +284,69 @@ def ds4hc_post_pre(X, coeffs_prev, layer_out, W_next, bias_next, *, rms_eps=1e-6
                               _ptr(logits), _ptr(workspace), ws_bytes, _stream(stream)),
            "ds4hc_post_pre")
     return X_out, layer_in, coeffs, logits
+
+
+def ds4hc_partials_workspace_bytes(params: Params, T: int, dtype: int) -> int:
+    return int(load().ds4hc_partials_workspace_bytes(ctypes.byref(params), int(T), int(dtype)))
+
+
+def ds4hc_partials_raw(params, T, dtype, X_share, W_share, partials, ws, ws_bytes, stream):
+    return load().ds4hc_partials(ctypes.byref(params), int(T), int(dtype), X_share, W_share,
+                                 partials, ws, int(ws_bytes), stream)
+
+
+def ds4hc_combine_raw(params, d_total, T, dtype, G, partials, bias, X_share, layer_out_share,
+                      layer_in_share, coeffs, X_out_share, stream):
+    return load().ds4hc_combine(ctypes.byref(params), int(d_total), int(T), int(dtype), int(G),
+                                partials, bias, X_share, layer_out_share, layer_in_share, coeffs,
+                                X_out_share, stream)
+
+
+def ds4hc_partials(X_share, W_share, *, flags=0, partials=None, workspace=None, stream=None):
+    """One column share: X_share [T, n, d_s], W_share [m, n*d_s] -> partials [T, m+1]
+    (unnormalised fn dots, then the sum of squares)."""
+    torch = _torch()
+    T, n, ds = X_share.shape
+    m = 2 * n + n * n
+    dt = _state_code(X_share)
+    p = make_params(n, ds, 1e-6, 20, flags)
+    _need(X_share, (T, n, ds), X_share.dtype, "X_share")
+    _need(W_share, (m, n * ds), torch.float16, "W_share")
+    if partials is None:
+        partials = torch.empty((T, m + 1), dtype=torch.float32, device=X_share.device)
+    need = ds4hc_partials_workspace_bytes(p, T, dt)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X_share.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(ds4hc_partials_raw(p, T, dt, _ptr(X_share), _ptr(W_share), _ptr(partials),
+                              _ptr(workspace), ws_bytes, _stream(stream)), "ds4hc_partials")
+    return partials
+
+
+def ds4hc_combine(partials, bias, X_share, layer_out_share, d_total, *, rms_eps=1e-6,
+                  sinkhorn_iters=20, coeffs=None, want_coeffs=True, layer_in_share=None,
+                  X_out_share=None, stream=None):
+    """partials [G, T, m+1] of all shares -> (layer_in_share, coeffs or None, X_out_share)."""
+    torch = _torch()
+    T, n, ds = X_share.shape
+    m = 2 * n + n * n
+    G = partials.shape[0]
+    dt = _state_code(X_share)
+    p = make_params(n, ds, rms_eps, sinkhorn_iters, 0)
+    _need(partials, (G, T, m + 1), torch.float32, "partials")
+    _need(bias, (m,), torch.float32, "bias")
+    _need(X_share, (T, n, ds), X_share.dtype, "X_share")
+    _need(layer_out_share, (T, ds), X_share.dtype, "layer_out_share")
+    if layer_in_share is None:
+        layer_in_share = torch.empty((T, ds), dtype=X_share.dtype, device=X_share.device)
+    if coeffs is None and want_coeffs:
+        coeffs = torch.empty((T, m), dtype=torch.float32, device=X_share.device)
+    if X_out_share is None:
+        X_out_share = torch.empty_like(X_share)
+    _check(ds4hc_combine_raw(p, d_total, T, dt, G, _ptr(partials), _ptr(bias), _ptr(X_share),
+                             _ptr(layer_out_share), _ptr(layer_in_share), _ptr(coeffs),
+                             _ptr(X_out_share), _stream(stream)), "ds4hc_combine")
+    return layer_in_share, coeffs, X_out_share
 
 
 def ds4hc_sinkhorn(logits_res, *, iters=20, H=None, stream=None):

@@ -245,6 +245,104 @@ ds4hc_status ds4hc_post_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype,
     return e == hipSuccess ? DS4HC_OK : hip_fail(e);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Split-over-d partials: the tile kernel where it fits and T is large, else
+// split-K chunks of the share (workspace) summed into [T][m+1].
+ds4hc_status make_partials_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *out) {
+    const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
+    const uint32_t force = p->flags & FORCE_FLAGS;
+    if (force == DS4HC_FLAG_FORCE_ROWRES) return DS4HC_ERR_UNSUPPORTED;
+    const bool fits_tile = ds4hc::tile_steps(d, dt) <= ds4hc::tile_max_steps();
+    Plan pl{ds4hc::PATH_SPLITK, 0, 0};
+    if (force == DS4HC_FLAG_FORCE_TILE || (force == 0 && T > SPLITK_MAX_T && fits_tile)) {
+        if (!fits_tile) return DS4HC_ERR_UNSUPPORTED;
+        pl.path = ds4hc::PATH_TILE;
+    } else {
+        pl.P = ds4hc::splitk_chunks(n, d, dt);
+        const uint64_t tg = (uint64_t)(T + 3) / 4;
+        if (tg * 64u > MAX_WORK_ITEMS || pl.P > 0xFFFF || (uint64_t)T * 64u > MAX_WORK_ITEMS)
+            return DS4HC_ERR_UNSUPPORTED;
+        pl.ws_bytes = (uint64_t)pl.P * (uint64_t)T * (uint64_t)(m + 1) * sizeof(float);
+    }
+    *out = pl;
+    return DS4HC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ds4hc_status ds4hc_partials(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X_share,
+                            const uint16_t *W_share, float *partials, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    ds4hc_status st = check_params(p, T, dtype);
+    if (st != DS4HC_OK || T == 0) return st;
+    if (!X_share || !W_share || !partials) return DS4HC_ERR_INVALID_ARG;
+    if (!aligned(X_share, 16) || !aligned(W_share, 16) || !aligned(partials, 4) ||
+        (workspace && !aligned(workspace, 4)))
+        return DS4HC_ERR_INVALID_ARG;
+    Plan pl;
+    st = make_partials_plan(p, T, dtype, &pl);
+    if (st != DS4HC_OK) return st;
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return DS4HC_ERR_INVALID_ARG;
+    const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
+    const uint64_t sb = (uint64_t)state_bytes(dtype), K = (uint64_t)n * d, uT = (uint64_t)T;
+    const Range rX{X_share, uT * K * sb}, rW{W_share, (uint64_t)m * K * 2};
+    const Range rP{partials, uT * (m + 1) * 4}, rws{pl.ws_bytes ? workspace : nullptr, pl.ws_bytes};
+    if (overlap(rP, rX) || overlap(rP, rW) || overlap(rP, rws) || overlap(rws, rX) || overlap(rws, rW))
+        return DS4HC_ERR_INVALID_ARG;
+    ds4hc::FusedArgs a{n, d, (int)dtype, p->sinkhorn_iters, T, p->rms_eps, X_share, W_share, nullptr,
+                       nullptr, nullptr, nullptr, partials, nullptr, static_cast<float *>(workspace)};
+    const hipError_t e = ds4hc::launch_partials(a, pl.path, stream);
+    return e == hipSuccess ? DS4HC_OK : hip_fail(e);
+}
+
+size_t ds4hc_partials_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype) {
+    if (check_params(p, T, dtype) != DS4HC_OK) return 0;
+    Plan pl;
+    if (make_partials_plan(p, T, dtype, &pl) != DS4HC_OK) return 0;
+    return (size_t)pl.ws_bytes;
+}
+
+ds4hc_status ds4hc_combine(const ds4hc_params *p, int32_t d_total, int64_t T, ds4hc_dtype dtype,
+                           int32_t G, const float *partials, const float *bias, const void *X_share,
+                           const void *layer_out_share, void *layer_in_share, float *coeffs_opt,
+                           void *X_out_share, hipStream_t stream) {
+    ds4hc_status st = check_params(p, T, dtype);
+    if (st != DS4HC_OK) return st;
+    if (d_total < p->d || d_total % 8 != 0 || G < 1 || G > 0xFFFF) return DS4HC_ERR_INVALID_ARG;
+    if (T == 0) return DS4HC_OK;
+    if (!partials || !bias || !X_share || !layer_out_share || !layer_in_share || !X_out_share)
+        return DS4HC_ERR_INVALID_ARG;
+    if (!aligned(X_share, 16) || !aligned(layer_out_share, 16) || !aligned(layer_in_share, 16) ||
+        !aligned(X_out_share, 16) || !aligned(partials, 4) || !aligned(bias, 4) ||
+        (coeffs_opt && !aligned(coeffs_opt, 4)))
+        return DS4HC_ERR_INVALID_ARG;
+    const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
+    const uint64_t sb = (uint64_t)state_bytes(dtype), K = (uint64_t)n * d, uT = (uint64_t)T;
+    const uint64_t cb = (uint64_t)(d + 64 * vec_elems(dtype) - 1) / (64 * vec_elems(dtype));
+    if (cb > 0xFFFFu || uT * 64u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
+    const Range rP{partials, (uint64_t)G * uT * (m + 1) * 4}, rb{bias, (uint64_t)m * 4};
+    const Range rX{X_share, uT * K * sb}, rlo{layer_out_share, uT * d * sb};
+    const Range rli{layer_in_share, uT * d * sb}, rc{coeffs_opt, uT * m * 4}, rXo{X_out_share, uT * K * sb};
+    const Range all[] = {rP, rb, rX, rlo, rli, rc, rXo};
+    constexpr int FIRST_OUT = 4, N_ALL = 7;
+    for (int a = FIRST_OUT; a < N_ALL; ++a) {
+        for (int b = 0; b < N_ALL; ++b) {
+            if (a == b) continue;
+            const bool in_place = ((a == 6 && b == 2) || (a == 2 && b == 6)) && X_out_share == X_share;
+            if (!in_place && overlap(all[a], all[b])) return DS4HC_ERR_INVALID_ARG;
+        }
+    }
+    ds4hc::FusedArgs a{n, d, (int)dtype, p->sinkhorn_iters, T, p->rms_eps, X_share, nullptr, bias,
+                       layer_out_share, layer_in_share, coeffs_opt, nullptr, X_out_share, nullptr};
+    const hipError_t e = ds4hc::launch_combine(a, d_total, G, partials, stream);
+    return e == hipSuccess ? DS4HC_OK : hip_fail(e);
+}
+
 size_t ds4hc_post_pre_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype) {
     if (check_params(p, T, dtype) != DS4HC_OK) return 0;
     PostPrePlan pp;

@@ -35,7 +35,10 @@ constexpr int ROWRES_THREADS = 256;
 constexpr int ROWRES_WAVES = ROWRES_THREADS / 64;
 constexpr int SPLITK_TOKENS = 4;   // tokens per partials workgroup
 
-enum : int { MODE_PRE = 0, MODE_FUSED = 1 };
+// MODE_PARTIALS (tile kernel only): write each token's unnormalised fn dots
+// and sum of squares, [T][m + 1] through the logits pointer, for one share of
+// the columns; no gates, Sinkhorn or pass 2 (the split-over-d exchange point).
+enum : int { MODE_PRE = 0, MODE_FUSED = 1, MODE_PARTIALS = 2 };
 
 // Largest number of column chunks (256*V columns each) a row-resident
 // instance keeps in registers without spilling to scratch on gfx950.
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
 
     // bias of the logit row this thread finishes in every tile, loaded once
     // (a load inside the loop would make the compiler drain every load in flight)
-    const float bias_row = tid < TILE_TOKENS * M ? bias[tid % M] : 0.f;
+    const float bias_row = MODE != MODE_PARTIALS && tid < TILE_TOKENS * M ? bias[tid % M] : 0.f;
 
     int ring_pos = 0;  // ring slot of unit 0 of the current tile
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -646,15 +649,22 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
             float s = zred[0][tt][row];
 #pragma unroll
             for (int w = 1; w < TILE_WAVES; ++w) s += zred[w][tt][row];
-            const float z = s * inv_r + bias_row;
-            zs[tt][row] = z;
             const size_t tk = tile0 + tt;
-            if (logits && tk < (size_t)T) logits[tk * M + row] = z;
+            if constexpr (MODE == MODE_PARTIALS) {
+                if (tk < (size_t)T) {
+                    logits[tk * (M + 1) + row] = s;
+                    if (row == 0) logits[tk * (M + 1) + M] = sst;
+                }
+            } else {
+                const float z = s * inv_r + bias_row;
+                zs[tt][row] = z;
+                if (logits && tk < (size_t)T) logits[tk * M + row] = z;
+            }
         }
         __syncthreads();
 
         // ---- phase 4: gates and Sinkhorn for the four tokens (wave 0) ----
-        if (wave == 0) {
+        if (MODE != MODE_PARTIALS && wave == 0) {
             constexpr int NN = N * N;
             const int grp = ln / NN, e = ln % NN, tt = grp % TILE_TOKENS;
             const float h = sinkhorn_lane_dpp<N>(zs[tt][2 * N + e], iters);
@@ -707,7 +717,8 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                 for (int i = 1; i < N; ++i) s = fmaf(pre[i], x[i][e], s);
                 li[e] = s;
             }
-            buf_store_vec<DT>(lir, col_ok ? d_voff + cs * STEP * SBYTES : OOB_OFFSET, li);
+            if constexpr (MODE != MODE_PARTIALS)
+                buf_store_vec<DT>(lir, col_ok ? d_voff + cs * STEP * SBYTES : OOB_OFFSET, li);
             if constexpr (MODE == MODE_FUSED) {
 #pragma unroll
                 for (int i = 0; i < N; ++i) {
@@ -786,6 +797,25 @@ __global__ __launch_bounds__(64) void hc_partials_kernel(int d, int T, const voi
             ws[((size_t)blockIdx.y * T + t) * (M + 1) + lane] = v;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split-over-d partials for small T: the split-K chunk partials of one column
+// share summed in chunk order into out[t][0..M] (dots, then sum of squares).
+// Grid (T), one wavefront.
+// ---------------------------------------------------------------------------
+template <int N>
+__global__ __launch_bounds__(64) void hc_chunk_sum_kernel(int T, int P, const float *__restrict__ ws,
+                                                          float *__restrict__ out) {
+    constexpr int M = n_logits(N);
+    const int lane = threadIdx.x;
+    const size_t t = blockIdx.x;
+    if (lane > M) return;
+    const float *p = ws + t * (M + 1) + lane;
+    const size_t stride = (size_t)T * (M + 1);
+    float tot = 0.f;
+    for (int c = 0; c < P; ++c) tot += p[(size_t)c * stride];
+    out[t * (M + 1) + lane] = tot;
 }
 
 // ---------------------------------------------------------------------------
@@ -879,7 +909,7 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
 // ---------------------------------------------------------------------------
 template <int N, int DT, int MODE>
 __global__ __launch_bounds__(64) void hc_finish_kernel(
-    int d, int T, int P, float eps, int iters, const void *__restrict__ X,
+    int d, int kfull, int T, int P, float eps, int iters, const void *__restrict__ X,
     const float *__restrict__ bias, const float *__restrict__ ws, const void *__restrict__ layer_out,
     void *__restrict__ layer_in, float *__restrict__ coeffs, float *__restrict__ logits, void *X_out) {
     constexpr int V = StateVec<DT>::V;
@@ -905,7 +935,7 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
         for (; c < P; ++c) tot += p[(size_t)c * stride];
     }
     const float ssum = __shfl(tot, M, 64);
-    const float r = sqrtf(ssum / (float)K + eps);
+    const float r = sqrtf(ssum / (float)kfull + eps);  // kfull: all n*d columns, also when X is a share
     float z = 0.f;
     if (lane < M) z = tot / r + bias[lane];
     const bool writer = blockIdx.y == 0;
@@ -1104,7 +1134,7 @@ static hipError_t launch_splitk_n(const FusedArgs &a, hipStream_t s) {
                                  a.W, a.ws);
     if (e != hipSuccess) return e;
     const dim3 g2((unsigned)a.T, (unsigned)((a.d + 64 * V - 1) / (64 * V)));
-    return launch_kernel(hc_finish_kernel<N, DT, MODE>, g2, dim3(64), s, a.d, (int)a.T, P, a.eps,
+    return launch_kernel(hc_finish_kernel<N, DT, MODE>, g2, dim3(64), s, a.d, N * a.d, (int)a.T, P, a.eps,
                          a.iters, a.X, a.bias, (const float *)a.ws, a.layer_out, a.layer_in,
                          a.coeffs, a.logits, a.X_out);
 }
@@ -1168,7 +1198,7 @@ static hipError_t launch_post_pre_n(const FusedArgs &a, const float *coeffs_prev
     if (e != hipSuccess) return e;
     // the pre-mix reads X' back from X_out; no post update here
     const dim3 g2((unsigned)a.T, (unsigned)P2);
-    return launch_kernel(hc_finish_kernel<N, DT, MODE_PRE>, g2, dim3(64), s, a.d, (int)a.T, P2,
+    return launch_kernel(hc_finish_kernel<N, DT, MODE_PRE>, g2, dim3(64), s, a.d, N * a.d, (int)a.T, P2,
                          a.eps, a.iters, (const void *)a.X_out, a.bias, (const float *)a.ws,
                          (const void *)nullptr, a.layer_in, a.coeffs, a.logits, (void *)nullptr);
 }
@@ -1198,6 +1228,55 @@ hipError_t launch_post_pre(const FusedArgs &a, const float *coeffs_prev, bool on
     case 4: DS4HC_PP(4);
     }
 #undef DS4HC_PP
+    return hipErrorInvalidValue;
+}
+
+template <int N, int DT>
+static hipError_t launch_partials_n(const FusedArgs &a, int path, hipStream_t s) {
+    if (path == PATH_TILE) return launch_tile_n<N, DT, MODE_PARTIALS>(tile_steps(a.d, DT), a, s);
+    const int P = splitk_chunks(N, a.d, DT);
+    const dim3 g1((unsigned)((a.T + SPLITK_TOKENS - 1) / SPLITK_TOKENS), (unsigned)P);
+    hipError_t e = launch_kernel(hc_partials_kernel<N, DT>, g1, dim3(64), s, a.d, (int)a.T, a.X,
+                                 a.W, a.ws);
+    if (e != hipSuccess) return e;
+    return launch_kernel(hc_chunk_sum_kernel<N>, dim3((unsigned)a.T), dim3(64), s, (int)a.T, P,
+                         (const float *)a.ws, a.logits);
+}
+
+hipError_t launch_partials(const FusedArgs &a, int path, hipStream_t s) {
+#define DS4HC_PA(NN)                                                                             \
+    return a.dt == DT_F32 ? launch_partials_n<NN, DT_F32>(a, path, s)                            \
+                          : launch_partials_n<NN, DT_BF16>(a, path, s)
+    switch (a.n) {
+    case 1: DS4HC_PA(1);
+    case 2: DS4HC_PA(2);
+    case 4: DS4HC_PA(4);
+    }
+#undef DS4HC_PA
+    return hipErrorInvalidValue;
+}
+
+template <int N, int DT>
+static hipError_t launch_combine_n(const FusedArgs &a, int d_total, int G, const float *partials,
+                                   hipStream_t s) {
+    constexpr int V = StateVec<DT>::V;
+    const dim3 g2((unsigned)a.T, (unsigned)((a.d + 64 * V - 1) / (64 * V)));
+    return launch_kernel(hc_finish_kernel<N, DT, MODE_FUSED>, g2, dim3(64), s, a.d, N * d_total,
+                         (int)a.T, G, a.eps, a.iters, a.X, a.bias, partials, a.layer_out,
+                         a.layer_in, a.coeffs, a.logits, a.X_out);
+}
+
+hipError_t launch_combine(const FusedArgs &a, int d_total, int G, const float *partials,
+                          hipStream_t s) {
+#define DS4HC_CO(NN)                                                                             \
+    return a.dt == DT_F32 ? launch_combine_n<NN, DT_F32>(a, d_total, G, partials, s)             \
+                          : launch_combine_n<NN, DT_BF16>(a, d_total, G, partials, s)
+    switch (a.n) {
+    case 1: DS4HC_CO(1);
+    case 2: DS4HC_CO(2);
+    case 4: DS4HC_CO(4);
+    }
+#undef DS4HC_CO
     return hipErrorInvalidValue;
 }
 

@@ -41,6 +41,13 @@ hipError_t launch_sinkhorn(int n, int iters, int64_t T, const float *Z, float *H
 // post(l) + pre(l+1): one pass (split-K chunks over columns, then the combining
 // kernel) or post then pre on `path`. a.X = X_l, a.layer_out = layer_out_l,
 // a.X_out = X_{l+1}, a.W/bias/layer_in/coeffs/logits = site l+1.
+// Split over d: a.X / a.W = one column share (a.d = its width), partial sums to
+// a.logits as [T][m + 1]; path PATH_TILE or PATH_SPLITK (workspace a.ws).
+hipError_t launch_partials(const FusedArgs &a, int path, hipStream_t s);
+// Combine G shares' partials [G][T][m + 1] in share order, then gates, Sinkhorn
+// and pass 2 on the share a.X (width a.d) of a row n * d_total long.
+hipError_t launch_combine(const FusedArgs &a, int d_total, int G, const float *partials,
+                          hipStream_t s);
 int post_pre_chunks(int d, int dt);
 hipError_t launch_post_pre(const FusedArgs &a, const float *coeffs_prev, bool one_pass, int path,
                            hipStream_t s);

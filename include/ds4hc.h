@@ -184,6 +184,40 @@ ds4hc_status ds4hc_post_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype,
 /* Workspace bytes ds4hc_post_pre needs for these arguments (0 if none or invalid). */
 size_t ds4hc_post_pre_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype);
 
+/*
+ * Split over d (one GPU's share of the columns of every stream; the exchange
+ * point of a tensor-parallel split, shown on one GPU). The op's only coupling
+ * across columns is the 2n + n^2 fn dot products and the sum of squares of
+ * each token row, so a share can emit those partial sums, the shares exchange
+ * them ([T, m + 1] floats per share: an all-gather), and each share finishes
+ * its own columns. p->d is the share's width d_s (d_s % 8 == 0).
+ *
+ * ds4hc_partials -- per token, over the share's columns:
+ *   partials[t][j] = sum_k W_share[j][k] x_share[k]  (j < m, unnormalised)
+ *   partials[t][m] = sum_k x_share[k]^2
+ *   X_share   [T, n, d_s]    state dtype   (read)
+ *   W_share   [m, n * d_s]   float16 bits  (read) W's columns i*d + share, per stream i
+ *   partials  [T, m + 1]     float32       (written)
+ *   workspace >= ds4hc_partials_workspace_bytes(p, T, dtype) bytes
+ */
+ds4hc_status ds4hc_partials(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X_share,
+                            const uint16_t *W_share, float *partials, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+size_t ds4hc_partials_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype);
+
+/*
+ * ds4hc_combine -- sums the G shares' partials [G, T, m + 1] in share order
+ * (deterministic; every share that combines the same partials gets bitwise the
+ * same coefficients), then z = dots / r + bias with r over all n * d_total
+ * columns, the gates, the Sinkhorn, and pass 2 on this share: layer_in_share
+ * = pre-mix, X_out_share = H . X_share + post (x) layer_out_share (may be
+ * exactly X_share). coeffs_opt [T, m] may be NULL. d_total >= p->d.
+ */
+ds4hc_status ds4hc_combine(const ds4hc_params *p, int32_t d_total, int64_t T, ds4hc_dtype dtype,
+                           int32_t G, const float *partials, const float *bias, const void *X_share,
+                           const void *layer_out_share, void *layer_in_share, float *coeffs_opt,
+                           void *X_out_share, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char *ds4hc_status_string(ds4hc_status s);
 

@@ -250,3 +250,39 @@ def test_post_pre_overlaps_workspace_and_in_place():
                     ws=None) == B.DS4HC_OK
     # in place is allowed: validation passes, so without a GPU the launch fails (ERR_HIP)
     assert post_pre(p, X_out=fake(0)) == B.DS4HC_ERR_HIP
+
+
+def test_partials_workspace_bytes():
+    p = B.make_params(4, 1024)   # a quarter share of d = 4096
+    P = (4 * 1024) // 256
+    assert B.ds4hc_partials_workspace_bytes(p, 1, B.DS4HC_F32) == P * 1 * 25 * 4
+    assert B.ds4hc_partials_workspace_bytes(p, 4096, B.DS4HC_F32) == 0   # tile kernel, partials mode
+    pr = B.make_params(4, 1024, flags=B.DS4HC_FLAG_FORCE_ROWRES)
+    assert B.ds4hc_partials_workspace_bytes(pr, 8, B.DS4HC_F32) == 0      # unsupported -> 0
+
+
+@no_gpu_only
+def test_partials_and_combine_validation():
+    p = B.make_params(4, 1024)
+    f = fake
+    # partials: null pointers, small workspace, overlap of the output with X
+    assert B.ds4hc_partials_raw(p, 8, 0, None, f(1), f(2), f(3), 1 << 30, None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_partials_raw(p, 8, 0, f(0), f(1), None, f(3), 1 << 30, None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_partials_raw(p, 8, 0, f(0), f(1), f(2), f(3), 16, None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_partials_raw(p, 8, 0, f(0), f(1), f(0, 64), f(3), 1 << 30, None) == B.DS4HC_ERR_INVALID_ARG
+    assert B.ds4hc_partials_raw(B.make_params(4, 1024, flags=B.DS4HC_FLAG_FORCE_ROWRES), 8, 0, f(0),
+                                f(1), f(2), f(3), 1 << 30, None) == B.DS4HC_ERR_UNSUPPORTED
+    assert B.ds4hc_partials_raw(p, 0, 0, None, None, None, None, 0, None) == B.DS4HC_OK
+
+    def comb(d_total=4096, G=4, **over):
+        a = dict(P=f(0), b=f(1), X=f(2), lo=f(3), li=f(4), c=f(5), Xo=f(6))
+        a.update(over)
+        return B.ds4hc_combine_raw(p, d_total, 8, 0, G, a["P"], a["b"], a["X"], a["lo"], a["li"],
+                                   a["c"], a["Xo"], None)
+    assert comb(d_total=1000) == B.DS4HC_ERR_INVALID_ARG      # d_total < share width
+    assert comb(d_total=4100) == B.DS4HC_ERR_INVALID_ARG      # d_total % 8
+    assert comb(G=0) == B.DS4HC_ERR_INVALID_ARG
+    assert comb(b=None) == B.DS4HC_ERR_INVALID_ARG
+    assert comb(li=f(2, 16)) == B.DS4HC_ERR_INVALID_ARG       # layer_in inside X_share
+    assert comb(Xo=f(2, 16)) == B.DS4HC_ERR_INVALID_ARG       # shifted in-place
+    assert comb(Xo=f(2)) == B.DS4HC_ERR_HIP                   # exact in place passes validation

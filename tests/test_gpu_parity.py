@@ -424,3 +424,41 @@ def test_decode_chain_43_layers_post_pre():
     ref = oracle.chain(wl.state_to_f64(case.X, case.dtype), case.chain_W, case.bias, case.chain_noise)
     e2e = assert_close_rows(torch_to_f64(X), ref[-1], 1e-4, "post_pre chain end to end")
     say(f"    end-to-end {e2e:.2e}")
+
+
+# ------------------------------------------------------------------ split over d (one GPU's share)
+
+def _shares(case, G):
+    torch = torch_mod()
+    X, W, b, lo = case_to_device(case)
+    n, d, m = case.n, case.d, case.m
+    ds = d // G
+    Wr = W.reshape(m, n, d)
+    sh = []
+    for g in range(G):
+        cols = slice(g * ds, (g + 1) * ds)
+        sh.append((X[:, :, cols].contiguous(), Wr[:, :, cols].reshape(m, n * ds).contiguous(),
+                   lo[:, cols].contiguous()))
+    return X, W, b, lo, sh
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("G,n,d", [(2, 4, 4096), (4, 4, 4096), (2, 2, 528)])
+@pytest.mark.parametrize("T", [1, 5, 700])
+def test_split_over_d(dtype, G, n, d, T):
+    """G column shares: partials per share, the [G, T, m+1] exchange, then each share
+    combines and finishes its own columns. The assembled result is the whole op
+    (checked against the oracle); every share computes bitwise the same coefficients."""
+    torch = torch_mod()
+    case = wl.make_random(40 + G + T, T, n, d, dtype)
+    X, W, b, lo, sh = _shares(case, G)
+    say(f"[gpu] split over d: G={G} T={T} n={n} d={d} {dtype}")
+    P = torch.stack([B.ds4hc_partials(xs, ws) for xs, ws, _ in sh])
+    outs = [B.ds4hc_combine(P, b, xs, los, d) for xs, _, los in sh]
+    torch.cuda.synchronize()
+    for li_g, c_g, _ in outs[1:]:
+        assert torch.equal(c_g, outs[0][1])
+    li = torch.cat([o[0] for o in outs], dim=1)
+    xo = torch.cat([o[2] for o in outs], dim=2)
+    got = (torch_to_f64(li), outs[0][1].cpu().numpy().astype(np.float64), torch_to_f64(xo))
+    check_full(case, got, f"split d G={G} T={T}")
