@@ -161,6 +161,53 @@ def sweep_paths(Ts=(1, 2, 3, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096),
                   flush=True)
 
 
+def split_share(G, steps, warmup):
+    """One GPU's share (d / G columns of every stream) of the prefill workload:
+    ds4hc_partials on the share, then ds4hc_combine with all G shares' partials
+    (the exchange itself is not timed: on one GPU the shares' partials are local)."""
+    import torch
+    from deepseek_v4_hyper_amd import binding as B
+    from deepseek_v4_hyper_amd import workloads as wl
+    c = wl.make_prefill(0)
+    T, n, d = c.T, c.n, c.d
+    m = 2 * n + n * n
+    ds = d // G
+    X, W, b, lo = to_device(c)
+    Xs = X[:, :, :ds].contiguous()
+    Ws = W.reshape(m, n, d)[:, :, :ds].reshape(m, n * ds).contiguous()
+    los = lo[:, :ds].contiguous()
+    P = torch.stack([B.ds4hc_partials(Xs, Ws) for _ in range(G)])
+    li = torch.empty((T, ds), device="cuda")
+    cf = torch.empty((T, m), device="cuda")
+    xo = torch.empty_like(Xs)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("partials", lambda: B.ds4hc_partials(Xs, Ws, partials=P[0])),
+                     ("combine", lambda: B.ds4hc_combine(P, b, Xs, los, d, coeffs=cf, layer_in_share=li,
+                                                         X_out_share=xo))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / steps
+    # bytes one share must move: partials reads X_s and W_s, writes [T, m+1]; combine reads
+    # the G partials, X_s and layer_out_s, writes X'_s, layer_in_s and the coefficients
+    bp = T * n * ds * 4 + m * n * ds * 2 + T * (m + 1) * 4
+    bc = G * T * (m + 1) * 4 + 2 * T * n * ds * 4 + 2 * T * ds * 4 + T * m * 4
+    for name, by in (("partials", bp), ("combine", bc)):
+        print(json.dumps({"split_d": G, "share_columns": ds, "T": T, "n_hc": n, "d": d, "dtype": "f32",
+                          "kernel": name, "us": res[name], "algorithmic_bytes": by,
+                          "GB_per_s": by / (res[name] * 1e-6) / 1e9}), flush=True)
+    tot = res["partials"] + res["combine"]
+    print(json.dumps({"split_d": G, "share_columns": ds, "T": T, "kernel": "share total", "us": tot,
+                      "tokens_per_s_per_share": T / (tot * 1e-6),
+                      "GB_per_s": (bp + bc) / (tot * 1e-6) / 1e9}), flush=True)
+
+
 def decode_chain(sites=86, d=4096, n=4, reps=20):
     """Decode-token chain of `sites` HC sites (attention and FFN per layer, 43 layers),
     T = 1, each site with its own f16 weight; the layer body is the stand-in
@@ -265,6 +312,9 @@ def main():
     ap.add_argument("--chain", action="store_true",
                     help="instead of the benchmark line: the 86-site decode chain (T=1, n=4, d=4096, "
                          "fp32), eager and HIP-graph replay, two calls per site vs one-pass post+pre")
+    ap.add_argument("--split-d", type=int, default=0, metavar="G",
+                    help="instead of the benchmark line: one GPU's share of a split over d into G "
+                         "column shares at the prefill shape: ds4hc_partials and ds4hc_combine timed")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: time every kernel path of ds4hc_fused over "
                          "T = 1..4096 (verify recipe, n=4, d=4096, fp32), one JSON line per (T, path)")
@@ -285,6 +335,9 @@ def main():
         return
     if args.chain:
         decode_chain()
+        return
+    if args.split_d:
+        split_share(args.split_d, args.steps, args.warmup)
         return
     cases = [make_case(args.workload, s) for s in range(args.sets)]
     c0 = cases[0]
