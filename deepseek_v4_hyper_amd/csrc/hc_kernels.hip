@@ -27,6 +27,7 @@
 #include <atomic>
 
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 namespace ds4hc {
@@ -215,10 +216,13 @@ __global__ __launch_bounds__(ROWRES_THREADS) void hc_rowres_kernel(
 //
 // W (the same for every tile) streams from L2 through a ring of unit-sized
 // slots in LDS, one ring per wave, filled by direct buffer->LDS loads that
-// run RING - 1 units ahead of the MFMAs and straight on into the next tile.
-// The next tile's rows are loaded into each column step's registers as soon
-// as the post update has consumed them, so HBM reads of tile k+1 overlap the
-// reductions, the Sinkhorn and the stores of tile k.
+// run RING - 1 units ahead of the MFMAs. The ring drains at the end of each
+// projection, and its LDS then takes the next tile's rows of the first STAGED
+// column steps straight from HBM, so those loads run during the reductions
+// and the Sinkhorn, while the registers still hold the current tile. Pass 2
+// moves the staged rows into each column step's registers as soon as the
+// post update has consumed them, restarts the ring for the next tile, and
+// loads the remaining steps' rows from HBM into their registers.
 //
 // Column step j of wave w covers STEP = 16*V columns of every stream:
 // columns (w + 8j)*STEP + b*V .. +V-1 for token t = lane % 4, so every lane
@@ -359,6 +363,21 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
         : "memory");
 }
 
+// The same load with the non-temporal cache policy, for state rows (read once).
+__device__ __forceinline__ void lds_dma16_nt(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base,
+                                             int voff, int soff) {
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+}
+
 // Wait until at most n vector-memory operations of this wave are outstanding.
 // Vector memory operations complete in issue order, so every operation older
 // than the last n is then complete.
@@ -368,6 +387,43 @@ __device__ __forceinline__ void wait_vm_at_most() {
     // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] at [15:14]
     constexpr int enc = (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
     asm volatile("s_waitcnt %0" : : "n"(enc) : "memory");
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E - 1, in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Loads a wave of the tile kernel has issued after the weight loads of unit u
+// when it reaches unit u's wait, at least (U units per tile, a ring of RING
+// slots, LOADS loads per unit; the ring is refilled only with units of the
+// same tile and started afresh for every tile):
+//  * u < RING: loaded by the tile's prologue, followed by the prologue's
+//    later units and the refills issued at units 0 .. u - 1 (unit v refills
+//    unit v + RING while that is < U);
+//  * u >= RING: loaded as the refill at unit u - RING, followed by the
+//    refills issued at units u - RING + 1 .. u - 1 that exist.
+// Capped at 63, the most the counter holds.
+constexpr int tile_unit_wait(int u, int U, int RING, int LOADS) {
+    const int after = u < RING ? LOADS * (RING - 1 - u) + LOADS * (u < U - RING ? u : U - RING)
+                               : LOADS * (RING - 1 < U - 1 - u ? RING - 1 : U - 1 - u);
+    return after < 63 ? after : 63;
+}
+
+// wait_vm_at_most<(S - 1 - j) * P>() for a step j < S that is a constant only
+// after loop unrolling (the S comparisons fold to the one wait).
+template <int S, int P, int J = 0>
+__device__ __forceinline__ void wait_vm_for_step(int j) {
+    if constexpr (J < S) {
+        if (j == J)
+            wait_vm_at_most<(S - 1 - J) * P>();
+        else
+            wait_vm_for_step<S, P, J + 1>(j);
+    }
 }
 
 // Sum over the 16 lanes of a DPP row that share lane % 4 (blocks of a row):
@@ -436,6 +492,11 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
     constexpr int RING = RING_CAP < U ? RING_CAP : U;
     constexpr int SBYTES = DT == DT_F32 ? 4 : 2;
     static_assert(RING >= 1 && RING * SLOT <= TILE_RING_BYTES, "weight ring");
+    // Column steps of the next tile's rows staged in this wave's ring area
+    // while the ring is idle (one 1 KiB load per stream and step).
+    constexpr int STAGE_FIT = RING * SLOT / (N * 1024);
+    constexpr int STAGED = STAGE_FIT < CS ? STAGE_FIT : CS;
+    static_assert(STAGED >= 1, "staging area");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -507,7 +568,6 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
     // (a load inside the loop would make the compiler drain every load in flight)
     const float bias_row = MODE != MODE_PARTIALS && tid < TILE_TOKENS * M ? bias[tid % M] : 0.f;
 
-    int ring_pos = 0;  // ring slot of unit 0 of the current tile
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const bool has_next = tile + (int)gridDim.x < ntiles;
         const size_t tile0 = (size_t)tile * TILE_TOKENS;
@@ -543,15 +603,14 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
         for (int g = 0; g < G; ++g) acc[g] = (float4_t){0.f, 0.f, 0.f, 0.f};
         int S = 140;  // |x| * 2^S < 2^14 for every x seen so far
         float ss = 0.f;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int slot = ring_pos + u % RING;
-            slot = slot >= RING ? slot - RING : slot;
-            // Unit u's loads are complete once no more vector-memory
-            // operations are outstanding than were issued after them: the
-            // refills of the next RING - 1 units (some of them the next
-            // tile's). Anything else issued since only makes this stricter.
-            wait_vm_at_most<LOADS * (RING - 1)>();
+        static_for<0, U>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            constexpr int slot = u % RING;
+            // Unit u's loads are complete once no more vector-memory loads
+            // are outstanding than were issued after them (loads complete in
+            // issue order): see tile_unit_wait. Anything else issued since
+            // only makes this stricter.
+            wait_vm_at_most<tile_unit_wait(u, U, RING, LOADS)>();
             HalfVec<V> w[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -607,15 +666,14 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                     acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, hi[sb], acc[g], 0, 0, 0);
                     acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, lo[sb], acc[g], 0, 0, 0);
                 }
-            // Refill this slot once this wave's reads of it are done: unit
-            // u + RING of this tile, or of the next one. W is the same for
-            // every tile, so the last tile refills too (the units go unused);
-            // that keeps the count of loads in flight the same for every unit.
-            const int nu = u + RING;
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            issue_unit(nu < U ? nu : nu - U, slot, dl, wlane, wcol);
-        }
-        ring_pos = (ring_pos + U) % RING;
+            // Refill this slot, once this wave's reads of it are done, with
+            // unit u + RING of this tile. The ring is not carried into the next
+            // tile: it holds the next tile's rows in between (below).
+            if constexpr (u + RING < U) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                issue_unit(u + RING, slot, dl, wlane, wcol);
+            }
+        });
 
         // layer_out for the post update: issued now, consumed after the reductions
         // and the Sinkhorn, whose latency it hides.
@@ -627,6 +685,24 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                 const int cs = wave + TILE_WAVES * j;
                 const int voff = bv < dl - cs * STEP ? d_voff : OOB_OFFSET;
                 lov[j] = buf_load_vec<DT>(lr, voff, cs * STEP * SBYTES);
+            }
+        }
+
+        // The ring has drained. Its LDS takes the next tile's rows of the
+        // first STAGED column steps, by direct loads that stream in during the
+        // reductions and the Sinkhorn; the registers still hold this tile.
+        // (Past the last tile the loads return zeros that go unused.)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's ring reads are done
+        {
+            const __amdgpu_buffer_rsrc_t xs = tile_rsrc(X, K, has_next ? tile + (int)gridDim.x : tile);
+#pragma unroll
+            for (int j = 0; j < STAGED; ++j) {
+                const int cs = wave + TILE_WAVES * j;
+                const int voff = bv < dl - cs * STEP && has_next ? x_voff : OOB_OFFSET;
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+                    lds_dma16_nt(xs, ring_base + (uint32_t)((j * N + i) * 1024), voff,
+                                 (i * dl + cs * STEP) * SBYTES);
             }
         }
 
@@ -739,7 +815,27 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                     buf_store_vec<DT>(xor_, col_ok ? x_voff + (i * d + cs * STEP) * SBYTES : OOB_OFFSET, o);
                 }
             }
-            {
+            if (j < STAGED) {
+                // Staged rows: step j's loads are complete once no more loads
+                // are outstanding than the staged loads issued after them
+                // (loads complete in issue order; stores since only add).
+                wait_vm_for_step<STAGED, N>(j);
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    const unsigned char *src = &wring[wave][0][0] + (j * N + i) * 1024 + 16 * ln;
+                    if constexpr (DT == DT_F32)
+                        xv[i][j].raw = *reinterpret_cast<const float4 *>(src);
+                    else
+                        xv[i][j].raw = *reinterpret_cast<const uint4 *>(src);
+                }
+                if (j == STAGED - 1) {
+                    // the staged rows are in registers: the next tile's first
+                    // RING weight units go into the ring
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                    for (int u = 0; u < RING; ++u) issue_unit(u, u, dl, wlane, wcol);
+                }
+            } else {
                 // (zeros past the last tile: no branch around the loads)
                 const int voff = col_ok && has_next ? x_voff : OOB_OFFSET;
 #pragma unroll
