@@ -141,41 +141,28 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Register-resident Sinkhorn. Lanes form groups of N*N; lane l of a group
 // holds Z[i][j] with i = (l % N^2) / N, j = l % N. All 64 lanes must call it.
 // Returns H[i][j] after: M = exp(Z - rowmax Z), then `iters` x (divide by row
-// sums, then by column sums).
-template <int N>
-__device__ __forceinline__ float sinkhorn_lane(float z, int iters) {
-    float mx = z;
-#pragma unroll
-    for (int s = 1; s < N; s <<= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, s, 64));
-    float m = expf(z - mx);
-    for (int it = 0; it < iters; ++it) {
-        float rs = m;
-#pragma unroll
-        for (int s = 1; s < N; s <<= 1)
-            rs += __shfl_xor(rs, s, 64);
-        m = m / rs;
-        float cs = m;
-#pragma unroll
-        for (int s = N; s < N * N; s <<= 1)
-            cs += __shfl_xor(cs, s, 64);
-        m = m / cs;
-    }
-    return m;
-}
-
-// Same result as sinkhorn_lane, with the lane exchanges done by DPP (no LDS
-// crossbar traffic). Row reductions (over j) are xor butterflies inside a
-// quad; column reductions (over i) for n = 4 rotate the 16-lane row by 8 and
-// then 4 lanes. Every lane of a row (column) ends with the same sum bits.
+// sums, then by column sums). The lane exchanges are DPP (no LDS crossbar
+// traffic): row reductions (over j) are xor butterflies inside a quad; column
+// reductions (over i) for n = 4 rotate the 16-lane row by 8 and then 4 lanes.
+// Every lane of a row (column) ends with the same sum bits.
+//
+// Each normalisation multiplies by the hardware reciprocal of the sum
+// (v_rcp_f32, within 1 ulp) instead of dividing: the 40 normalisations of a
+// 20-iteration Sinkhorn are one serial chain, and the IEEE division sequence
+// (scale, reciprocal, Newton steps, fix-up) made up most of its latency. The
+// error stays a few float32 ulps of each entry; sums of powers of two (the
+// uniform and permutation cases) are still exact. A product with the
+// reciprocal can exceed 1 by an ulp where an entry is its whole row or column
+// sum (a quotient cannot), so the result is clamped to 1; the comparison keeps
+// NaN as NaN.
 template <int N>
 __device__ __forceinline__ float sinkhorn_lane_dpp(float z, int iters) {
     static_assert(N == 1 || N == 2 || N == 4, "n_hc");
     if constexpr (N == 1) {
         float m = expf(z - z);
         for (int it = 0; it < iters; ++it) {
-            m = m / m;
-            m = m / m;
+            m = m * __builtin_amdgcn_rcpf(m);
+            m = m * __builtin_amdgcn_rcpf(m);
         }
         return m;
     } else {
@@ -187,7 +174,7 @@ __device__ __forceinline__ float sinkhorn_lane_dpp(float z, int iters) {
         for (int it = 0; it < iters; ++it) {
             float rs = m + dpp_mov<XOR1>(m);
             if constexpr (N == 4) rs = rs + dpp_mov<XOR2>(rs);
-            m = m / rs;
+            m = m * __builtin_amdgcn_rcpf(rs);
             float cs;
             if constexpr (N == 4) {
                 // rows i and i+2 first: then every lane of a column adds the
@@ -197,9 +184,9 @@ __device__ __forceinline__ float sinkhorn_lane_dpp(float z, int iters) {
             } else {
                 cs = m + dpp_mov<XOR2>(m);
             }
-            m = m / cs;
+            m = m * __builtin_amdgcn_rcpf(cs);
         }
-        return m;
+        return m > 1.0f ? 1.0f : m;
     }
 }
 

@@ -242,6 +242,23 @@ def test_sinkhorn_random(n, iters):
     assert_coeffs(H, oracle.sinkhorn(Z, iters), "sinkhorn")
 
 
+def test_sinkhorn_entries_within_unit_interval():
+    # logits at the stress workload's scale (std 20): every entry of H lies in
+    # [0, 1] (an entry equal to its row or column sum must not round above 1),
+    # and a NaN logit turns its own matrix into NaN and no other
+    torch = torch_mod()
+    rng = np.random.Generator(np.random.PCG64(7))
+    Z = (rng.standard_normal((20000, 4, 4)) * 20).astype(np.float32)
+    Z[5, 1, 2] = np.nan
+    for iters in (1, 2, 20):
+        say(f"[gpu] ds4hc_sinkhorn n=4 iters={iters} logit std 20, one NaN matrix")
+        H = B.ds4hc_sinkhorn(torch.from_numpy(Z).cuda(), iters=iters).cpu().numpy()
+        assert np.isnan(H[5]).all()
+        rest = np.delete(H, 5, axis=0)
+        assert np.all((rest >= 0) & (rest <= 1))
+        assert_coeffs(rest, oracle.sinkhorn(np.delete(Z, 5, axis=0), iters), "sinkhorn")
+
+
 def test_sinkhorn_closed_forms():
     torch = torch_mod()
     P = np.zeros((4, 4))
