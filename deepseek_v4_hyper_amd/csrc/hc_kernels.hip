@@ -745,7 +745,31 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
         }
         __syncthreads();
 
-        // ---- phase 4: gates and Sinkhorn for the four tokens (wave 0) ----
+        const __amdgpu_buffer_rsrc_t lir = tile_rsrc(layer_in, (size_t)d, tile);
+        // ---- phase 4: gates and Sinkhorn for the four tokens (wave 0). For a
+        // float32 state the other waves compute their pre gates themselves (the
+        // same function on the same logits, so the same bits) and store the
+        // pre-mix meanwhile: prefill 153.4 -> 150.9 us on MI355X. (For bfloat16
+        // the extra unpacking made that instance spill registers.)
+        constexpr bool EARLY_PREMIX = MODE != MODE_PARTIALS && DT == DT_F32;
+        if (EARLY_PREMIX && wave != 0) {
+            float pre_w[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) pre_w[i] = logistic(zs[t][i]);
+#pragma unroll
+            for (int j = 0; j < CS; ++j) {
+                const int cs = wave + TILE_WAVES * j;
+                float li[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    float s = pre_w[0] * vec_get<DT>(xv[0][j], e);
+#pragma unroll
+                    for (int i = 1; i < N; ++i) s = fmaf(pre_w[i], vec_get<DT>(xv[i][j], e), s);
+                    li[e] = s;
+                }
+                buf_store_vec<DT>(lir, bv < dl - cs * STEP ? d_voff + cs * STEP * SBYTES : OOB_OFFSET, li);
+            }
+        }
         if (MODE != MODE_PARTIALS && wave == 0) {
             constexpr int NN = N * N;
             const int grp = ln / NN, e = ln % NN, tt = grp % TILE_TOKENS;
@@ -779,7 +803,6 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
         for (int j = 0; j < CS; ++j)
 #pragma unroll
             for (int i = 0; i < N; ++i) launder<DT>(xv[i][j]);
-        const __amdgpu_buffer_rsrc_t lir = tile_rsrc(layer_in, (size_t)d, tile);
         const __amdgpu_buffer_rsrc_t xor_ = tile_rsrc(X_out, K, tile);
         const __amdgpu_buffer_rsrc_t xnext = tile_rsrc(X, K, has_next ? tile + (int)gridDim.x : tile);
 #pragma unroll
@@ -799,7 +822,8 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                 for (int i = 1; i < N; ++i) s = fmaf(pre[i], x[i][e], s);
                 li[e] = s;
             }
-            if constexpr (MODE != MODE_PARTIALS)
+            // (with EARLY_PREMIX, waves 1..7 stored theirs during the Sinkhorn)
+            if (MODE != MODE_PARTIALS && (!EARLY_PREMIX || wave == 0))
                 buf_store_vec<DT>(lir, col_ok ? d_voff + cs * STEP * SBYTES : OOB_OFFSET, li);
             if constexpr (MODE == MODE_FUSED) {
 #pragma unroll
