@@ -119,6 +119,20 @@ def copy_calibration(nbytes=1 << 30):
           flush=True)
 
 
+def warm_gpu(ms=60.0):
+    """Keep the GPU busy for about `ms` milliseconds (a 256 MiB device copy in a
+    loop) so that the measurements after it run at steady clocks."""
+    import torch
+    a = torch.empty(1 << 26, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+
 def sweep_paths(Ts=(1, 2, 3, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096), steps=200, warmup=20):
     """Per-call time of each kernel path of ds4hc_fused across T (the split-K / tile
     crossover), warm: the same inputs every call, as in a decode or verify loop."""
@@ -208,7 +222,7 @@ def split_share(G, steps, warmup):
                       "GB_per_s": (bp + bc) / (tot * 1e-6) / 1e9}), flush=True)
 
 
-def decode_chain(sites=86, d=4096, n=4, reps=20):
+def decode_chain(sites=86, d=4096, n=4, reps=50):
     """Decode-token chain of `sites` HC sites (attention and FFN per layer, 43 layers),
     T = 1, each site with its own f16 weight; the layer body is the stand-in
     layer_out = 0.5 * layer_in + noise (one elementwise kernel). Variants: two
@@ -334,12 +348,15 @@ def main():
 
     B.load()
     if args.sweep:
+        warm_gpu()
         sweep_paths()
         return
     if args.chain:
+        warm_gpu()
         decode_chain()
         return
     if args.split_d:
+        warm_gpu()
         split_share(args.split_d, args.steps, args.warmup)
         return
     cases = [make_case(args.workload, s) for s in range(args.sets)]
