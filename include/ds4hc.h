@@ -42,6 +42,10 @@
  *   - State dtype (X, layer_in, layer_out, X_out): float32 or bfloat16.
  *     Coefficients, logits and bias are float32; W is IEEE float16.
  *     Arithmetic is float32 with one round-to-nearest-even at each store.
+ *     The Sinkhorn normalises by multiplying with the hardware reciprocal
+ *     of each row or column sum (within 1 ulp of 1/sum) rather than by a
+ *     correctly rounded division, and clamps each entry of H to at most 1
+ *     (a NaN stays NaN); H is within a few float32 ulps of the divided result.
  *   - Every path is deterministic: no floating-point atomics, fixed
  *     reduction orders. Repeated calls on equal inputs give equal bits.
  *   - T = 0 returns DS4HC_OK once the scalar arguments are valid, without
