@@ -80,8 +80,9 @@ def to_device(case):
     return X, W, b, lo
 
 
-def cpu_baseline(case, runs=3):
-    """fp64 oracle on the full workload, all host cores; median of `runs`."""
+def cpu_baseline(case, min_runs=3, min_seconds=5.0, max_runs=50):
+    """fp64 oracle on the full workload, all host cores; the median of repeated
+    runs (at least `min_runs`, and until about `min_seconds` of oracle time)."""
     import oracle
     from deepseek_v4_hyper_amd import workloads as wl
     X = wl.state_to_f64(case.X, case.dtype)
@@ -90,10 +91,11 @@ def cpu_baseline(case, runs=3):
     b = case.bias.astype(np.float64)
     oracle.fused(X[:8], W, b, lo[:8], case.eps, case.iters)  # load + warm
     times = []
-    for _ in range(runs):
+    while len(times) < max_runs and (len(times) < min_runs or sum(times) < min_seconds):
         t0 = time.perf_counter()
         oracle.fused(X, W, b, lo, case.eps, case.iters)
         times.append(time.perf_counter() - t0)
+    runs = len(times)
     sec = float(np.median(times))
     return {"value": case.T / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
