@@ -207,12 +207,14 @@ __global__ __launch_bounds__(ROWRES_THREADS) void hc_rowres_kernel(
 // The fn projection of a tile is a [m x K] . [K x 4] product. One
 // 4x4x4_16b instruction is 16 independent 4x4x4 products (block b = lane/4):
 // A_b = 4 rows of W x 4 consecutive k, B_b = those 4 k x the 4 tokens. Lane
-// 4b + t supplies token t's B column and W row t of the group's A. x~ = x/r
-// is split exactly into f16 hi + lo (hi = f16(x~), lo = f16(x~ - hi)); hi and
-// lo are two MFMAs on the same A accumulating into one result, so hi + lo
-// carries x~ to ~2^-23 relative, products are exact and accumulation is
-// fp32. |x~| <= sqrt(K), so f16 cannot overflow. Each W element fetched from
-// L2 feeds all four tokens.
+// 4b + t supplies token t's B column and W row t of the group's A. The lane's
+// x, scaled by a power of two 2^S that puts its largest |x| in [2^13, 2^14)
+// (so f16 cannot overflow), is split exactly into f16 hi + lo (hi = f16(x~),
+// lo = f16(x~ - hi)); hi and lo are two MFMAs on the same A accumulating into
+// one result, so hi + lo carries x~ to ~2^-23 relative, products are exact and
+// accumulation is fp32; 2^-S and 1/r are applied to the reduced sums. For a
+// bfloat16 state hi alone carries x~ (lo is skipped; see the projection).
+// Each W element fetched from L2 feeds all four tokens.
 //
 // W (the same for every tile) streams from L2 through a ring of unit-sized
 // slots in LDS, one ring per wave, filled by direct buffer->LDS loads that
@@ -650,13 +652,21 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                     xt[e] = __builtin_amdgcn_ldexpf(xr[4 * sb + e], S);
                     hi[sb][e] = (_Float16)xt[e];
                 }
-                // lo must be formed from the very bits the MFMA consumes as hi:
-                // left free, the compiler rounds x~ to f16 twice with two
-                // instructions that break ties differently, and hi + lo misses
-                // x~ by one f16 ulp on exact ties.
-                pin_half4(hi[sb]);
+                // A bfloat16 x has 8 significant bits, which f16 holds exactly
+                // down to 2^-17 (its subnormals included); the lane's largest
+                // scaled value is at least 2^13, so hi misses x~ only for values
+                // more than 2^30 below it, by at most 2^-25 = 2^-38 of it. lo is
+                // then zero or negligible, and its MFMAs are skipped (stress
+                // workload: the same bits, 618.2 -> 605.9 us on MI355X).
+                if constexpr (DT == DT_F32) {
+                    // lo must be formed from the very bits the MFMA consumes as
+                    // hi: left free, the compiler rounds x~ to f16 twice with two
+                    // instructions that break ties differently, and hi + lo
+                    // misses x~ by one f16 ulp on exact ties.
+                    pin_half4(hi[sb]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lo[sb][e] = (_Float16)(xt[e] - (float)hi[sb][e]);
+                    for (int e = 0; e < 4; ++e) lo[sb][e] = (_Float16)(xt[e] - (float)hi[sb][e]);
+                }
             }
 #pragma unroll
             for (int sb = 0; sb < SB; ++sb)
@@ -664,7 +674,8 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                 for (int g = 0; g < G; ++g) {
                     const half4_t a = half_sub4<V>(w[g], sb);
                     acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, hi[sb], acc[g], 0, 0, 0);
-                    acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, lo[sb], acc[g], 0, 0, 0);
+                    if constexpr (DT == DT_F32)
+                        acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, lo[sb], acc[g], 0, 0, 0);
                 }
             // Refill this slot, once this wave's reads of it are done, with
             // unit u + RING of this tile. The ring is not carried into the next

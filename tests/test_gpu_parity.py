@@ -132,6 +132,24 @@ def test_tile_several_tiles_per_workgroup(n, d, dtype):
     check_full(case, run_fused(case, FLAGS["tile"]), f"tile x3 n={n} d={d} {dtype}")
 
 
+@pytest.mark.parametrize("path", ["tile", "rowres", "splitk"])
+def test_bf16_wide_dynamic_range(path):
+    """bfloat16 rows whose elements span 2^-60 .. 2^0 (each scaled by its own
+    random power of two): the tile kernel's projection uses only the f16 hi part
+    of a bfloat16 element, which is exact down to 2^30 below the lane's largest
+    value, so even rows like these match the oracle within the bfloat16
+    tolerance, with the coefficients within 2e-5."""
+    import dataclasses
+    rng = np.random.Generator(np.random.PCG64(77))
+    T, n, d = 2 * _cu_count() + 5, 4, 2048
+    base = wl.make_random(77, T, n, d, wl.BF16)
+    x = wl.bf16_bits_to_f32(base.X).astype(np.float64)
+    x = x * np.exp2(-rng.integers(0, 61, size=x.shape))
+    case = dataclasses.replace(base, name="bf16_wide_range",
+                               X=wl.f32_to_bf16_bits(x.astype(np.float32)))
+    check_full(case, run_fused(case, FLAGS[path]), f"bf16 wide range/{path}")
+
+
 def test_tile_prefill_recipe_several_tiles_in_place_and_pre():
     """Prefill recipe at T = 8 * CUs + 3 on the tile path: fused against the
     oracle on every element, in place (X_out = X) bitwise equal to out of
