@@ -341,6 +341,27 @@ def test_deterministic_repeats():
     assert len(digests) == 1
 
 
+@pytest.mark.parametrize("workload", ["prefill", "stress"])
+def test_deterministic_repeats_full_size(workload):
+    """The benchmark's own launch configuration (prefill: 4 tiles per tile-kernel
+    workgroup; stress: 16), run 3 times: every output identical bit for bit."""
+    import hashlib
+    torch = torch_mod()
+    case = wl.make_prefill(5) if workload == "prefill" else wl.make_stress(5)
+    X, W, b, lo = case_to_device(case)
+    say(f"[gpu] 3 repeats of ds4hc_fused, {workload} T={case.T} d={case.d} {case.dtype}")
+    digests = set()
+    for _ in range(3):
+        outs = B.ds4hc_fused(X, W, b, lo)
+        torch.cuda.synchronize()
+        h = hashlib.sha256()
+        for o in outs:
+            h.update(o.contiguous().view(torch.uint8).cpu().numpy().tobytes())
+        digests.add(h.hexdigest())
+        del outs
+    assert len(digests) == 1
+
+
 def test_nan_row_stays_in_its_token():
     torch = torch_mod()
     case = wl.make_prefill(7, T=40)
