@@ -537,8 +537,20 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
             lds_dma16(wrsrc, ring_base + (uint32_t)(slot * SLOT + q * 1024), voff, soff);
         }
     };
-    auto lane_wlane = [&](int ln) { return (16 * ln / ROWB) * row_bytes + (16 * ln) % ROWB; };
-    auto lane_wcol = [&](int ln) { return ((16 * ln) % ROWB) / 2; };
+    // Bank swizzle of a slot: row r's bytes sit at r * ROWB + (c ^ wswz(r)).
+    // A unit read has lane 4b + t read row 4g + t at the same column for
+    // every t; with 128-byte rows (float32 state) rows t and t + 2, with
+    // 256-byte rows (bfloat16) all four rows would share banks (64 banks of
+    // 4 bytes). Exchanging row halves (quarters) by row makes each read
+    // conflict-free; the arithmetic is unchanged.
+    static_assert(ROWB == 128 || ROWB == 256, "weight row pitch");
+    auto wswz = [](int r) { return ROWB == 128 ? ((r >> 1) & 1) * 64 : (r & 3) * 64; };
+    // lane l's direct load puts the unit's bytes for slot offset 16 l (+ 1024 q)
+    auto lane_wlane = [&](int ln) {
+        const int r = 16 * ln / ROWB;
+        return r * row_bytes + (((16 * ln) % ROWB) ^ wswz(r));
+    };
+    auto lane_wcol = [&](int ln) { return (((16 * ln) % ROWB) ^ wswz(16 * ln / ROWB)) / 2; };
 
     // the first tile's first RING units, before anything else
 #pragma unroll
@@ -587,7 +599,7 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
         const int x_voff = (t * (int)K + bv) * SBYTES;
         const int d_voff = (t * dl + bv) * SBYTES;
         const int wlane = lane_wlane(ln), wcol = lane_wcol(ln);
-        const int wread = (t * ROWB + bv * 2);  // byte of row t's slice read by this lane
+        const int wread = t * ROWB + ((bv * 2) ^ wswz(t));  // byte of row t's slice read by this lane
 
         // ---- phase 2: fn matvec on MFMA, weights from the LDS ring ----
         // The projection runs on the raw rows and is normalised afterwards
