@@ -634,18 +634,31 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                 else
                     w[g].raw = *reinterpret_cast<const uint4 *>(src);
             }
-            if (u % N == 0) {
-                // the scale for the N units of this column step
-                const int eb = max_biased_exponent<DT, N>(xv, u / N);
+            // Scale updates. For a float32 state, two per tile: at unit 0 from
+            // the staged column steps, at the first unit of the other steps from
+            // those (whose rows have in practice all arrived by then, as that
+            // unit's weight refill queues behind them): prefill 147.4 -> 146.1
+            // us on MI355X, the same bits. For bfloat16 that form made the
+            // instance spill registers, so it updates at every column step.
+            constexpr bool TWO_SCALES = DT == DT_F32;
+            if constexpr (TWO_SCALES ? (u == 0 || u == STAGED * N) : (u % N == 0)) {
+                constexpr int j0 = TWO_SCALES ? (u == 0 ? 0 : STAGED) : u / N;
+                constexpr int j1 = TWO_SCALES ? (u == 0 ? STAGED : CS) : u / N + 1;
+                int eb = 0;
+#pragma unroll
+                for (int j = j0; j < j1; ++j) eb = max(eb, max_biased_exponent<DT, N>(xv, j));
                 // 2^(140 - eb) puts the largest |x| in [2^13, 2^14); for Inf or
                 // NaN the scale is tiny and Inf stays Inf, NaN stays NaN.
                 const int s_new = min(S, 140 - eb);
                 // Rescale unconditionally (by 2^0 when nothing changed): a
                 // branch here fragments the unrolled loop and costs registers.
+                // At unit 0 the accumulators are still zero.
+                if constexpr (u != 0) {
 #pragma unroll
-                for (int g = 0; g < G; ++g)
+                    for (int g = 0; g < G; ++g)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[g][r] = __builtin_amdgcn_ldexpf(acc[g][r], s_new - S);
+                        for (int r = 0; r < 4; ++r) acc[g][r] = __builtin_amdgcn_ldexpf(acc[g][r], s_new - S);
+                }
                 S = s_new;
             }
             const StateVec<DT> &xvu = xv[u % N][u / N];
