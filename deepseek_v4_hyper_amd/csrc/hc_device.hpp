@@ -38,6 +38,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Two float32 -> one word of two bfloat16 (a in the low half), each rounded to
+// nearest even: the same bits as two f32_to_bf16_bits, but one
+// v_cvt_pk_bf16_f32 instead of two conversions, a shift and an or.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+    const f2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2_t));
+}
+
 __device__ __forceinline__ float f16_lo(uint32_t u) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
 }
@@ -84,10 +94,10 @@ __device__ __forceinline__ void store_vec(void *base, size_t elem_off, const flo
             make_float4(f[0], f[1], f[2], f[3]);
     } else {
         uint4 u;
-        u.x = f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16);
-        u.y = f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16);
-        u.z = f32_to_bf16_bits(f[4]) | (f32_to_bf16_bits(f[5]) << 16);
-        u.w = f32_to_bf16_bits(f[6]) | (f32_to_bf16_bits(f[7]) << 16);
+        u.x = f32x2_to_bf16x2_bits(f[0], f[1]);
+        u.y = f32x2_to_bf16x2_bits(f[2], f[3]);
+        u.z = f32x2_to_bf16x2_bits(f[4], f[5]);
+        u.w = f32x2_to_bf16x2_bits(f[6], f[7]);
         *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + elem_off) = u;
     }
 }

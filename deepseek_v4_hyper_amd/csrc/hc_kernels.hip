@@ -332,10 +332,8 @@ __device__ __forceinline__ void buf_store_vec(__amdgpu_buffer_rsrc_t r, int voff
         u = (u32x4){__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
                     __float_as_uint(f[3])};
     } else {
-        u = (u32x4){f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16),
-                    f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16),
-                    f32_to_bf16_bits(f[4]) | (f32_to_bf16_bits(f[5]) << 16),
-                    f32_to_bf16_bits(f[6]) | (f32_to_bf16_bits(f[7]) << 16)};
+        u = (u32x4){f32x2_to_bf16x2_bits(f[0], f[1]), f32x2_to_bf16x2_bits(f[2], f[3]),
+                    f32x2_to_bf16x2_bits(f[4], f[5]), f32x2_to_bf16x2_bits(f[6], f[7])};
     }
     __builtin_amdgcn_raw_buffer_store_b128(u, r, voff, 0, CPOL_STREAM);
 }
