@@ -426,6 +426,17 @@ __device__ __forceinline__ void wait_vm_for_step(int j) {
     }
 }
 
+// Wave priority (s_setprio takes an immediate): 3 while a wave issues loads of
+// the state stream, otherwise `base` (0 or 1).
+__device__ __forceinline__ void set_wave_prio(bool high, bool base) {
+    if (high)
+        __builtin_amdgcn_s_setprio(3);
+    else if (base)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+
 // Sum over the 16 lanes of a DPP row that share lane % 4 (blocks of a row):
 // rotations by 4 and 8 lanes.
 __device__ __forceinline__ float row_sum_by4(float v) {
@@ -711,15 +722,26 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
 
         // layer_out for the post update: issued now, consumed after the reductions
         // and the Sinkhorn, whose latency it hides.
+        // Issue priority. The CU's vector-memory stream serves waves in
+        // priority order, then by age, so the older wave of each SIMD (0..3)
+        // used to get its whole pass 2 through first, and waves 4..7 - the
+        // tile's critical path - finished pass 2 and their projection ~9 us
+        // later. Every load of the state stream (layer_out, staged and HBM rows
+        // of the next tile) is issued at priority 3, so loads overtake queued
+        // stores, and waves 4..7 run pass 2 at priority 1. Prefill 146.6 ->
+        // 140.7 us, stress 598.3 -> 554.6 us on MI355X, the same bits.
+        const bool late_wave = wave >= TILE_WAVES / 2;
         StateVec<DT> lov[CS];
         if constexpr (MODE == MODE_FUSED) {
             const __amdgpu_buffer_rsrc_t lr = tile_rsrc(layer_out, (size_t)d, tile);
+            set_wave_prio(true, false);
 #pragma unroll
             for (int j = 0; j < CS; ++j) {
                 const int cs = wave + TILE_WAVES * j;
                 const int voff = bv < dl - cs * STEP ? d_voff : OOB_OFFSET;
                 lov[j] = buf_load_vec<DT>(lr, voff, cs * STEP * SBYTES);
             }
+            set_wave_prio(false, false);
         }
 
         // The ring has drained. Its LDS takes the next tile's rows of the
@@ -729,6 +751,7 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's ring reads are done
         {
             const __amdgpu_buffer_rsrc_t xs = tile_rsrc(X, K, has_next ? tile + (int)gridDim.x : tile);
+            set_wave_prio(true, false);
 #pragma unroll
             for (int j = 0; j < STAGED; ++j) {
                 const int cs = wave + TILE_WAVES * j;
@@ -738,6 +761,7 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
                     lds_dma16_nt(xs, ring_base + (uint32_t)((j * N + i) * 1024), voff,
                                  (i * dl + cs * STEP) * SBYTES);
             }
+            set_wave_prio(false, false);
         }
 
         // ---- phase 3: undo each lane's scale, sum the 16 blocks (DPP within
@@ -838,6 +862,7 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
 #pragma unroll
             for (int i = 0; i < N; ++i) launder<DT>(xv[i][j]);
         const __amdgpu_buffer_rsrc_t xor_ = tile_rsrc(X_out, K, tile);
+        set_wave_prio(false, late_wave);
         const __amdgpu_buffer_rsrc_t xnext = tile_rsrc(X, K, has_next ? tile + (int)gridDim.x : tile);
 #pragma unroll
         for (int j = 0; j < CS; ++j) {
@@ -896,10 +921,13 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
             } else {
                 // (zeros past the last tile: no branch around the loads)
                 const int voff = col_ok && has_next ? x_voff : OOB_OFFSET;
+                set_wave_prio(true, late_wave);
 #pragma unroll
                 for (int i = 0; i < N; ++i) xv[i][j] = buf_load_vec<DT>(xnext, voff, (i * dl + cs * STEP) * SBYTES);
+                set_wave_prio(false, late_wave);
             }
         }
+        set_wave_prio(false, false);
     }
     // no load into this workgroup's LDS may still be in flight when it ends
     wait_vm_at_most<0>();
