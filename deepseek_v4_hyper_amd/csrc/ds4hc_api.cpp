@@ -78,8 +78,8 @@ struct Plan {
 // Path for HC-pre / fused: split-K for small T (the fn weight dominates the
 // bytes and must be spread over many CUs), the one-token VALU kernel for
 // middling T, the persistent MFMA tile kernel for large T (measured on MI355X
-// at n = 4: 167 us against 259 us for the VALU kernel at T = 4096, d = 4096
-// float32, and 692 us against 1333 us at T = 16384, d = 7168 bfloat16), then
+// at n = 4: 141.5 us against 258 us for the VALU kernel at T = 4096, d = 4096
+// float32, and 557 us against 1333 us at T = 16384, d = 7168 bfloat16), then
 // the VALU kernel, then split-K where a row is too long for either.
 // Returns UNSUPPORTED if a forced path cannot take the shape or a launch
 // would not fit.

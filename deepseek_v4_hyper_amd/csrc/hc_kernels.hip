@@ -1,16 +1,24 @@
 // hc_kernels.hip -- HIP kernels of the DeepSeek-V4 hyper-connection op for
 // MI355X (gfx950) and their host-side launchers.
 //
-// Two paths compute the same op (see ds4hc.h for its definition):
+// Three paths compute the same op (see ds4hc.h for its definition); the
+// library picks one by T (thresholds from a measured sweep), and flags can
+// force any of them:
 //
-//  * row-resident (large T): one 256-thread workgroup per token. The token's
-//    n*d state is loaded once from HBM into registers, the RMS statistic and
-//    the m = 2n + n*n fn dot products are accumulated from it, reduced in a
-//    fixed order, the gates and the register-resident Sinkhorn run in one
-//    wavefront, and the pre-mix and post update are computed from the same
-//    registers. X is read once and X' written once: the HBM-bound minimum.
+//  * tile (T > 384): a persistent MFMA kernel, one 512-thread workgroup per
+//    CU striding over tiles of four tokens. A tile's rows live in registers,
+//    so X is read once and X' written once; the fn matvec runs on
+//    v_mfma_f32_4x4x4_16b_f16 with W streamed from L2 through per-wave LDS
+//    rings, and the drained rings stage half of the next tile's rows.
 //
-//  * split-K (small T, decode and speculative verify): the fn weight (m*K
+//  * row-resident (161 <= T <= 384, or rows too long for the tile kernel):
+//    one 256-thread workgroup per token; the token's n*d state is loaded once
+//    into registers, the RMS statistic and the m = 2n + n*n fn dot products
+//    are accumulated from it on the VALU, reduced in a fixed order, the gates
+//    and the register-resident Sinkhorn run in one wavefront, and the pre-mix
+//    and post update are computed from the same registers.
+//
+//  * split-K (T <= 160, decode and speculative verify): the fn weight (m*K
 //    float16, 768 KiB at d = 4096) dominates the bytes, so K is cut into
 //    chunks and many workgroups each read one chunk of W for all tokens,
 //    writing fixed-order partial sums to a caller workspace. A second kernel
@@ -19,8 +27,16 @@
 //    sites 86 times per token (lucebox-hub PR #494, Sinkhorn comment), so
 //    this path is about latency, not bandwidth.
 //
-// Arithmetic: float32 everywhere, f16 weights widened exactly, one RNE
-// rounding at each store of a bf16 state. No floating-point atomics.
+// Also here: the one-pass decode-chain step (post of one site and the split-K
+// part of the next), the two halves of the split over d (partial sums of a
+// column share; their share-order combine), the post update alone and the
+// Sinkhorn alone.
+//
+// Arithmetic: float32 accumulation with f16 weights widened exactly; the tile
+// kernel's products are exact (the scaled state split into f16 hi + lo; hi
+// alone for a bfloat16 state, exact to 2^-38 of the lane's largest value); the
+// Sinkhorn multiplies by the hardware reciprocal of each sum; one RNE rounding
+// at each store of a bf16 state. No floating-point atomics.
 #include "hc_device.hpp"
 #include "hc_launch.hpp"
 
