@@ -293,23 +293,6 @@ constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 // which would make the compiler drain all outstanding loads at the joins).
 constexpr int OOB_OFFSET = 0x7FFFFFF0;
 
-// W for one (column step, stream) unit: V float16 of row 4g + lane%4 per group.
-template <int V, int G>
-__device__ __forceinline__ void load_w_unit(HalfVec<V> (&w)[G], __amdgpu_buffer_rsrc_t rsrc,
-                                            int voff, int soff_base, int soff_group) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int soff = soff_base + g * soff_group;
-        if constexpr (V == 4) {
-            const uint2_t u = __builtin_bit_cast(
-                uint2_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, 0));
-            w[g].raw = make_uint2(u.x, u.y);
-        } else {
-            w[g].raw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
-        }
-    }
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              BUFFER_RSRC_WORD3);
