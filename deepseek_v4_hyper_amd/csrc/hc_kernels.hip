@@ -1106,18 +1106,30 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
     const size_t K = (size_t)N * d;
     __shared__ float cf[M];
 
+    // This lane's columns of X (and layer_out) for pass 2, loaded first: at
+    // decode sizes the kernel is latency-bound, and these loads then overlap
+    // the partial sums and the Sinkhorn instead of following them.
+    const int c0 = (blockIdx.y * 64 + lane) * V;
+    const bool col_ok = c0 < d;
+    StateVec<DT> xs[N], lvs;
+    if (col_ok) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) xs[i] = load_vec<DT>(X, t * K + (size_t)i * d + c0);
+        if constexpr (MODE == MODE_FUSED) lvs = load_vec<DT>(layer_out, t * d + c0);
+    }
+
     float tot = 0.f;
     if (lane <= M) {
         const float *p = ws + t * (M + 1) + lane;
         const size_t stride = (size_t)T * (M + 1);
-        // chunk order, eight loads in flight at a time
+        // chunk order, sixteen loads in flight at a time
         int c = 0;
-        for (; c + 8 <= P; c += 8) {
-            float v[8];
+        for (; c + 16 <= P; c += 16) {
+            float v[16];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = p[(size_t)(c + k) * stride];
+            for (int k = 0; k < 16; ++k) v[k] = p[(size_t)(c + k) * stride];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) tot += v[k];
+            for (int k = 0; k < 16; ++k) tot += v[k];
         }
         for (; c < P; ++c) tot += p[(size_t)c * stride];
     }
@@ -1140,15 +1152,12 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
     }
     __syncthreads();
 
-    const int c0 = (blockIdx.y * 64 + lane) * V;
-    if (c0 >= d) return;
+    if (!col_ok) return;
     float x[N][V];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const StateVec<DT> v = load_vec<DT>(X, t * K + (size_t)i * d + c0);
+    for (int i = 0; i < N; ++i)
 #pragma unroll
-        for (int e = 0; e < V; ++e) x[i][e] = vec_get<DT>(v, e);
-    }
+        for (int e = 0; e < V; ++e) x[i][e] = vec_get<DT>(xs[i], e);
     float li[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -1159,7 +1168,6 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
     }
     store_vec<DT>(layer_in, t * d + c0, li);
     if constexpr (MODE == MODE_FUSED) {
-        const StateVec<DT> lv = load_vec<DT>(layer_out, t * d + c0);
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             float o[V];
@@ -1168,7 +1176,7 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
                 float s = cf[2 * N + i * N] * x[0][e];
 #pragma unroll
                 for (int j = 1; j < N; ++j) s = fmaf(cf[2 * N + i * N + j], x[j][e], s);
-                o[e] = fmaf(cf[N + i], vec_get<DT>(lv, e), s);
+                o[e] = fmaf(cf[N + i], vec_get<DT>(lvs, e), s);
             }
             store_vec<DT>(X_out, t * K + (size_t)i * d + c0, o);
         }
