@@ -1007,13 +1007,37 @@ __global__ __launch_bounds__(64) void hc_chunk_sum_kernel(int T, int P, const fl
 
 // ---------------------------------------------------------------------------
 // One-pass chain step, split-K part: grid (ceil(T / SPLITK_TOKENS), P2), one
-// wavefront. Chunk p covers columns [p*64*V, (p+1)*64*V) of every stream, so a
-// lane holds all n streams of its V columns and can apply the previous site's
-// post update X' = H.X + post (x) layer_out itself (same operation order as
-// hc_post_kernel, so X' is bitwise what ds4hc_post writes). It stores X' and
-// writes the partial dots of the next site's fn projection and the partial
-// sum of squares of X' (as rounded to the state type) to ws[p][t][0..M].
+// wavefront. Chunk p covers columns [p*32*V, (p+1)*32*V) of every stream: lane
+// l = 32 g + c holds the V columns p*32*V + c*V .. of all n streams, so it can
+// apply the previous site's post update X' = H.X + post (x) layer_out itself
+// (same operation order as hc_post_kernel, so X' is bitwise what ds4hc_post
+// writes); the two 32-lane groups g hold the same columns and split the M fn
+// rows of the next site (rows g*RPW ..), and group 0 stores X'. At decode sizes
+// the step is bound by each CU's weight stream: chunks of 32 lanes spread W
+// over twice as many CUs as chunks of 64 (6.2 against 7.5 us at T = 1,
+// d = 4096, fp32), while 16-lane chunks, with 8-byte W loads per lane and X
+// read by four groups, take 9.1 us. Writes the partial dots of the next site's
+// fn projection and the partial sum of squares of X' (as rounded to the state
+// type) to ws[p][t][0..M].
 // ---------------------------------------------------------------------------
+constexpr int POSTPRE_LANES = 32;  // lanes per column chunk; two row groups per wave
+
+// Sum over the POSTPRE_LANES lanes of a column chunk (every lane gets the
+// total): within each 16-lane DPP row, then across row pairs by the gfx950 row
+// swap when a chunk spans two rows.
+__device__ __forceinline__ float chunk_sum(float v) {
+    static_assert(POSTPRE_LANES == 16 || POSTPRE_LANES == 32, "chunk of one or two DPP rows");
+    v += dpp_mov<0x128>(v);  // row_ror:8
+    v += dpp_mov<0x124>(v);  // row_ror:4
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (POSTPRE_LANES == 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    return v;
+}
+
 template <int N, int DT>
 __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
     int d, int T, const void *__restrict__ X, const float *__restrict__ coeffs_prev,
@@ -1021,9 +1045,14 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
     float *__restrict__ ws) {
     constexpr int V = StateVec<DT>::V;
     constexpr int M = n_logits(N);
+    constexpr int RG = 64 / POSTPRE_LANES;     // row groups
+    constexpr int RPW = (M + RG - 1) / RG;     // fn rows per group
     const int lane = threadIdx.x;
+    const int grp = lane / POSTPRE_LANES, cl = lane % POSTPRE_LANES;
+    const int row0 = grp * RPW;
+    const bool ss_group = grp == RG - 1;
     const size_t K = (size_t)N * d;
-    const int c0 = (blockIdx.y * 64 + lane) * V;
+    const int c0 = (blockIdx.y * POSTPRE_LANES + cl) * V;
     const bool ok = c0 < d;
     const int tbase = blockIdx.x * SPLITK_TOKENS;
 
@@ -1033,9 +1062,9 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
         if (t >= T) break;  // uniform across the wavefront
         const float *cp = coeffs_prev + (size_t)t * M;
         float x[N][V];
-        float acc[M + 1];
+        float acc[RPW + 1];
 #pragma unroll
-        for (int j = 0; j <= M; ++j) acc[j] = 0.f;
+        for (int j = 0; j <= RPW; ++j) acc[j] = 0.f;
         if (ok) {
             float xin[N][V];
 #pragma unroll
@@ -1055,7 +1084,9 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
                     for (int j = 1; j < N; ++j) s = fmaf(cp[2 * N + i * N + j], xin[j][e], s);
                     o[e] = fmaf(cp[N + i], vec_get<DT>(lv, e), s);
                 }
-                store_vec<DT>(X_out, (size_t)t * K + (size_t)i * d + c0, o);
+                // (the row groups read X in the same instruction: group 0's
+                // store cannot overtake another group's load)
+                if (grp == 0) store_vec<DT>(X_out, (size_t)t * K + (size_t)i * d + c0, o);
                 // the next site sees X' as stored (rounded to the state type)
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
@@ -1068,24 +1099,30 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
 #pragma unroll
             for (int i = 0; i < N; ++i) {
 #pragma unroll
-                for (int j = 0; j < M; ++j) {
+                for (int r = 0; r < RPW; ++r) {
+                    // rows past M (last group when 4 does not divide M) read
+                    // row M - 1 and are never stored: no branch around the
+                    // loads, so they all stay in flight together
+                    const int j = min(row0 + r, M - 1);
                     const HalfVec<V> w = load_half_vec<V>(W + (size_t)j * K + (size_t)i * d + c0);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) acc[j] = fmaf(half_get<V>(w, e), x[i][e], acc[j]);
+                    for (int e = 0; e < V; ++e) acc[r] = fmaf(half_get<V>(w, e), x[i][e], acc[r]);
                 }
 #pragma unroll
-                for (int e = 0; e < V; ++e) acc[M] = fmaf(x[i][e], x[i][e], acc[M]);
+                for (int e = 0; e < V; ++e) acc[RPW] = fmaf(x[i][e], x[i][e], acc[RPW]);
             }
         }
 #pragma unroll
-        for (int j = 0; j <= M; ++j) acc[j] = wave_sum(acc[j]);
-        if (lane <= M) {
+        for (int j = 0; j <= RPW; ++j) acc[j] = chunk_sum(acc[j]);
+        float *out = ws + ((size_t)blockIdx.y * T + t) * (M + 1);
+        if (cl < RPW && row0 + cl < M) {
             float v = acc[0];
 #pragma unroll
-            for (int j = 1; j <= M; ++j)
-                if (lane == j) v = acc[j];
-            ws[((size_t)blockIdx.y * T + t) * (M + 1) + lane] = v;
+            for (int j = 1; j < RPW; ++j)
+                if (cl == j) v = acc[j];
+            out[row0 + cl] = v;
         }
+        if (ss_group && cl == POSTPRE_LANES - 1) out[M] = acc[RPW];
     }
 }
 
@@ -1122,14 +1159,14 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
     if (lane <= M) {
         const float *p = ws + t * (M + 1) + lane;
         const size_t stride = (size_t)T * (M + 1);
-        // chunk order, sixteen loads in flight at a time
+        // chunk order, thirty-two loads in flight at a time
         int c = 0;
-        for (; c + 16 <= P; c += 16) {
-            float v[16];
+        for (; c + 32 <= P; c += 32) {
+            float v[32];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) v[k] = p[(size_t)(c + k) * stride];
+            for (int k = 0; k < 32; ++k) v[k] = p[(size_t)(c + k) * stride];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) tot += v[k];
+            for (int k = 0; k < 32; ++k) tot += v[k];
         }
         for (; c < P; ++c) tot += p[(size_t)c * stride];
     }
@@ -1386,13 +1423,15 @@ hipError_t launch_hc(const FusedArgs &a, bool fused, int path, hipStream_t s) {
 template <int N, int DT>
 static hipError_t launch_post_pre_n(const FusedArgs &a, const float *coeffs_prev, hipStream_t s) {
     constexpr int V = StateVec<DT>::V;
-    const int P2 = (a.d + 64 * V - 1) / (64 * V);
+    const int P2 = post_pre_chunks(a.d, DT);
     const dim3 g1((unsigned)((a.T + SPLITK_TOKENS - 1) / SPLITK_TOKENS), (unsigned)P2);
     hipError_t e = launch_kernel(hc_postpre_partials_kernel<N, DT>, g1, dim3(64), s, a.d, (int)a.T,
                                  a.X, coeffs_prev, a.layer_out, a.W, a.X_out, a.ws);
     if (e != hipSuccess) return e;
-    // the pre-mix reads X' back from X_out; no post update here
-    const dim3 g2((unsigned)a.T, (unsigned)P2);
+    // the pre-mix reads X' back from X_out; no post update here. The finish
+    // kernel sums the P2 chunk partials; its pass 2 takes 64 * V columns per
+    // workgroup.
+    const dim3 g2((unsigned)a.T, (unsigned)((a.d + 64 * V - 1) / (64 * V)));
     return launch_kernel(hc_finish_kernel<N, DT, MODE_PRE>, g2, dim3(64), s, a.d, N * a.d, (int)a.T, P2,
                          a.eps, a.iters, (const void *)a.X_out, a.bias, (const float *)a.ws,
                          (const void *)nullptr, a.layer_in, a.coeffs, a.logits, (void *)nullptr);
@@ -1400,7 +1439,7 @@ static hipError_t launch_post_pre_n(const FusedArgs &a, const float *coeffs_prev
 
 int post_pre_chunks(int d, int dt) {
     const int V = dt == DT_F32 ? 4 : 8;
-    return (d + 64 * V - 1) / (64 * V);
+    return (d + POSTPRE_LANES * V - 1) / (POSTPRE_LANES * V);
 }
 
 hipError_t launch_post_pre(const FusedArgs &a, const float *coeffs_prev, bool one_pass, int path,
