@@ -1128,10 +1128,13 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
 
 // ---------------------------------------------------------------------------
 // Split-K finish: grid (T, ceil(d / (64*V))), one wavefront. Combines the P
-// partials of token t in chunk order, computes logits, gates and Sinkhorn,
+// partials of token t in chunk order (PB loads in flight: 64 takes the 64
+// chunks of the decode pre at d = 4096 fp32 in one round, 8.08 -> 7.95 us at
+// T = 1; the one-pass chain step, with 32 chunks, is 0.2 us slower with the
+// larger batch's registers and keeps 32), computes logits, gates and Sinkhorn,
 // then the pre-mix (and post update) of 64*V columns.
 // ---------------------------------------------------------------------------
-template <int N, int DT, int MODE>
+template <int N, int DT, int MODE, int PB = 64>
 __global__ __launch_bounds__(64) void hc_finish_kernel(
     int d, int kfull, int T, int P, float eps, int iters, const void *__restrict__ X,
     const float *__restrict__ bias, const float *__restrict__ ws, const void *__restrict__ layer_out,
@@ -1159,14 +1162,15 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
     if (lane <= M) {
         const float *p = ws + t * (M + 1) + lane;
         const size_t stride = (size_t)T * (M + 1);
-        // chunk order, thirty-two loads in flight at a time
+        // chunk order, PB loads in flight at a time (the partials were
+        // written by other CUs: each round is a trip past this XCD's L2)
         int c = 0;
-        for (; c + 32 <= P; c += 32) {
-            float v[32];
+        for (; c + PB <= P; c += PB) {
+            float v[PB];
 #pragma unroll
-            for (int k = 0; k < 32; ++k) v[k] = p[(size_t)(c + k) * stride];
+            for (int k = 0; k < PB; ++k) v[k] = p[(size_t)(c + k) * stride];
 #pragma unroll
-            for (int k = 0; k < 32; ++k) tot += v[k];
+            for (int k = 0; k < PB; ++k) tot += v[k];
         }
         for (; c < P; ++c) tot += p[(size_t)c * stride];
     }
@@ -1432,7 +1436,7 @@ static hipError_t launch_post_pre_n(const FusedArgs &a, const float *coeffs_prev
     // kernel sums the P2 chunk partials; its pass 2 takes 64 * V columns per
     // workgroup.
     const dim3 g2((unsigned)a.T, (unsigned)((a.d + 64 * V - 1) / (64 * V)));
-    return launch_kernel(hc_finish_kernel<N, DT, MODE_PRE>, g2, dim3(64), s, a.d, N * a.d, (int)a.T, P2,
+    return launch_kernel(hc_finish_kernel<N, DT, MODE_PRE, 32>, g2, dim3(64), s, a.d, N * a.d, (int)a.T, P2,
                          a.eps, a.iters, (const void *)a.X_out, a.bias, (const float *)a.ws,
                          (const void *)nullptr, a.layer_in, a.coeffs, a.logits, (void *)nullptr);
 }
