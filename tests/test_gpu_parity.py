@@ -422,10 +422,11 @@ def _post_pre_case(seed, T, n, d, dtype):
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 @pytest.mark.parametrize("n,d", [(4, 4096), (2, 264), (1, 1032), (4, 2056)])
-@pytest.mark.parametrize("T", [1, 3, 37])
+@pytest.mark.parametrize("T", [1, 3, 37, 200])
 def test_post_pre_equals_post_then_pre(dtype, n, d, T):
-    """ds4hc_post_pre against ds4hc_post followed by ds4hc_pre (T = 1, 3: the one-pass
-    split-K kernels; T = 37: post then the tile path). X' must be bitwise what
+    """ds4hc_post_pre against ds4hc_post followed by ds4hc_pre (T = 1, 3, 37: the
+    one-pass split-K kernels, one or several token groups; T = 200: post, then the
+    row-resident pre on X'). X' must be bitwise what
     ds4hc_post writes; layer_in and coeffs are checked against the oracle's HC-pre
     of that X' and against the two-call path."""
     torch = torch_mod()
@@ -446,7 +447,7 @@ def test_post_pre_equals_post_then_pre(dtype, n, d, T):
     assert_close_rows(torch_to_f64(Xo), rxp, tol, "post_pre X'")
 
 
-@pytest.mark.parametrize("T", [2, 40])
+@pytest.mark.parametrize("T", [2, 40, 200])
 def test_post_pre_in_place(T):
     torch = torch_mod()
     case, nxt, X, c_prev, lo, Wn, bn = _post_pre_case(31, T, 4, 4096, wl.F32)
