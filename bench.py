@@ -8,8 +8,14 @@ prefill, T = 4096 tokens, n_hc = 4, d = 4096, float32 state.
     python bench.py [--steps K] [--warmup W] [--workload prefill|stress]
 
 Prints one JSON line. Three input sets are rotated so no step starts with its
-inputs warm in the 256 MiB last-level cache. The CPU baseline is the fp64
-oracle on the same workload (all host cores).
+inputs warm in the 256 MiB last-level cache. Before the warm-up steps the op
+runs for ~100 ms of wall time, so the timed steps see steady clocks however
+few warm-up steps are asked for. Besides the headline figures the line holds:
+the bandwidth of a plain 1 GiB device copy measured in the same process (and
+the op's fraction of it), the per-call latency of the decode-sized workloads
+(T=1, d=256 and T=4, d=4096) warm and with the caches flushed, and the CPU
+baseline: the fp64 oracle on the same workload with all host cores, and with
+one thread on a sample of it.
 """
 from __future__ import annotations
 
@@ -80,9 +86,37 @@ def to_device(case):
     return X, W, b, lo
 
 
-def cpu_baseline(case, min_runs=3, min_seconds=5.0, max_runs=50):
-    """fp64 oracle on the full workload, all host cores; the median of repeated
-    runs (at least `min_runs`, and until about `min_seconds` of oracle time)."""
+def cpu_info():
+    """Host CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return model, os.cpu_count(), usable
+
+
+def _time_oracle(fn, min_runs, min_seconds, max_runs):
+    times = []
+    while len(times) < max_runs and (len(times) < min_runs or sum(times) < min_seconds):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), len(times)
+
+
+def cpu_baseline(case, min_runs=3, min_seconds=5.0, max_runs=50, single_tokens=1024):
+    """fp64 oracle on the host: all cores on the whole workload (the median of
+    repeated runs, at least `min_runs` and until about `min_seconds` of oracle
+    time), and one thread on the first `single_tokens` tokens (median of 3)."""
     import oracle
     from deepseek_v4_hyper_amd import workloads as wl
     X = wl.state_to_f64(case.X, case.dtype)
@@ -90,17 +124,93 @@ def cpu_baseline(case, min_runs=3, min_seconds=5.0, max_runs=50):
     W = case.W.astype(np.float64)
     b = case.bias.astype(np.float64)
     oracle.fused(X[:8], W, b, lo[:8], case.eps, case.iters)  # load + warm
-    times = []
-    while len(times) < max_runs and (len(times) < min_runs or sum(times) < min_seconds):
-        t0 = time.perf_counter()
-        oracle.fused(X, W, b, lo, case.eps, case.iters)
-        times.append(time.perf_counter() - t0)
-    runs = len(times)
-    sec = float(np.median(times))
-    return {"value": case.T / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    all_threads = oracle.num_threads()
+    sec, runs = _time_oracle(lambda: oracle.fused(X, W, b, lo, case.eps, case.iters),
+                             min_runs, min_seconds, max_runs)
+    ts = min(single_tokens, case.T)
+    oracle.set_threads(1)
+    try:
+        sec1, runs1 = _time_oracle(lambda: oracle.fused(X[:ts], W, b, lo[:ts], case.eps, case.iters),
+                                   3, 0.0, 3)
+    finally:
+        oracle.set_threads(all_threads)
+    model, ncpu, usable = cpu_info()
+    return {"value": case.T / sec, "unit": "tokens/s", "cores": all_threads, "kind": "oracle",
             "sample": f"whole {case.name} workload (T={case.T}, n={case.n}, d={case.d}, "
-                      f"{case.dtype}), median of {runs} runs, {sec:.3f} s each"}
+                      f"{case.dtype}), median of {runs} runs, {sec:.3f} s each",
+            "single_thread": {"value": ts / sec1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"first {ts} tokens of the same workload, median of "
+                                        f"{runs1} runs, {sec1:.3f} s each"},
+            "cpu_model": model, "nproc": ncpu, "usable_cpus": usable}
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=20):
+    """Plain device copy (torch's elementwise copy kernel, read nbytes + write
+    nbytes) at steady clocks: GB/s of read + write bytes, median over reps."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for s, e in ev:
+        s.record()
+        b.copy_(a)
+        e.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([s.elapsed_time(e) for s, e in ev]))
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def latency_records(reps=101, flush_bytes=512 << 20):
+    """Microseconds per ds4hc_fused call for the two decode-sized workloads (the
+    single token, T=1, d=256, and the speculative-verify batch, T=4, d=4096):
+    warm (the same inputs call after call, W resident in the caches, as in a
+    decode loop) and cold (a 512 MiB buffer written between calls, flushing
+    the L2 and last-level caches). Each call is bracketed by its own HIP events
+    on the launch stream; the median over `reps` calls is reported."""
+    import torch
+    from deepseek_v4_hyper_amd import binding as B
+    from deepseek_v4_hyper_amd import workloads as wl
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out = []
+    for case in (wl.make_single(0), wl.make_verify(0)):
+        X, W, b, lo = to_device(case)
+        m = 2 * case.n + case.n * case.n
+        li = torch.empty((case.T, case.d), device="cuda")
+        cf = torch.empty((case.T, m), device="cuda")
+        xo = torch.empty_like(X)
+        params = B.make_params(case.n, case.d, case.eps, case.iters)
+        wsb = B.ds4hc_workspace_bytes(params, case.T, B.DS4HC_F32)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        ptr = [ctypes.c_void_p(t.data_ptr()) for t in (X, W, b, lo, li, cf, xo, ws)]
+
+        def call():
+            st = B.ds4hc_fused_raw(params, case.T, B.DS4HC_F32, *ptr[:7], ptr[7], wsb, sp)
+            if st != B.DS4HC_OK:
+                raise B.Ds4hcError(st, "ds4hc_fused")
+        rec = {"workload": case.name, "T": case.T, "n_hc": case.n, "d": case.d, "dtype": "f32"}
+        for mode in ("warm", "cold"):
+            for _ in range(10):
+                call()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for s, e in ev:
+                if mode == "cold":
+                    flush.fill_(1.0)
+                s.record(stream)
+                call()
+                e.record(stream)
+            torch.cuda.synchronize()
+            rec[f"{mode}_us"] = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3
+        out.append(rec)
+    del flush
+    return out
 
 
 def copy_calibration(nbytes=1 << 30):
@@ -133,6 +243,21 @@ def warm_gpu(ms=60.0):
         for _ in range(8):
             b.copy_(a)
         torch.cuda.synchronize()
+
+
+def warm_with(step, ms=100.0, batch=20):
+    """Run `step(i)` for about `ms` milliseconds of wall time: the GPU needs tens
+    of milliseconds of this load to reach its steady clocks, however few
+    warm-up steps the caller asks for."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(batch):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
 
 
 def sweep_paths(Ts=(1, 2, 3, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096), steps=200, warmup=20):
@@ -326,6 +451,10 @@ def main():
     ap.add_argument("--path", default="default", choices=["default", "rowres", "tile", "splitk"],
                     help="force one kernel path (default: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the copy-bandwidth and decode-latency measurements")
+    ap.add_argument("--warm-ms", type=float, default=100.0,
+                    help="milliseconds of untimed steps before the warm-up steps (steady clocks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for counter scaling)")
     ap.add_argument("--chain", action="store_true",
@@ -389,6 +518,8 @@ def main():
         if st != B.DS4HC_OK:
             raise B.Ds4hcError(st, "ds4hc_fused")
 
+    # time-based warm-up first (steady clocks), then the requested warm-up steps
+    warm_with(step, args.warm_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -402,6 +533,10 @@ def main():
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / args.steps
 
+    extras = {}
+    if not args.no_extras:
+        extras["copy_gbps"] = copy_bandwidth()
+        extras["latency"] = latency_records()
     if args.copy_calibration:
         copy_calibration()
 
@@ -434,6 +569,10 @@ def main():
                      "algorithmic_bytes_per_launch": alg,
                      "kernel": KERNEL_NAME[args.path]},
     }
+    if "copy_gbps" in extras:
+        rec["roofline"]["copy_gbps"] = extras["copy_gbps"]
+        rec["roofline"]["frac_of_copy"] = achieved / extras["copy_gbps"]
+        rec["latency_us"] = extras["latency"]
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(c0)
     print(json.dumps(rec), flush=True)

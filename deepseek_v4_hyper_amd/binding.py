@@ -8,6 +8,7 @@ the stream. There is no fallback: if the library is missing, calls raise.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -140,6 +141,22 @@ def ds4hc_sinkhorn_raw(T, n_hc, iters, logits_res, H, stream):
     return load().ds4hc_sinkhorn(int(T), int(n_hc), int(iters), logits_res, H, stream)
 
 
+def ds4hc_partials_workspace_bytes(params: Params, T: int, dtype: int) -> int:
+    return int(load().ds4hc_partials_workspace_bytes(ctypes.byref(params), int(T), int(dtype)))
+
+
+def ds4hc_partials_raw(params, T, dtype, X_share, W_share, partials, ws, ws_bytes, stream):
+    return load().ds4hc_partials(ctypes.byref(params), int(T), int(dtype), X_share, W_share,
+                                 partials, ws, int(ws_bytes), stream)
+
+
+def ds4hc_combine_raw(params, d_total, T, dtype, G, partials, bias, X_share, layer_out_share,
+                      layer_in_share, coeffs, X_out_share, stream):
+    return load().ds4hc_combine(ctypes.byref(params), int(d_total), int(T), int(dtype), int(G),
+                                partials, bias, X_share, layer_out_share, layer_in_share, coeffs,
+                                X_out_share, stream)
+
+
 # ------------------------------------------------------------------ torch-tensor calls
 
 def _torch():
@@ -166,6 +183,19 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which the binding allocates what it passes to a call on `stream`.
+
+    The caching allocator ties a block to the stream that was current when it
+    was allocated, and hands it out again once it is freed with no regard for
+    work still queued on other streams. Buffers the binding creates (workspace,
+    default outputs) are therefore allocated with the kernels' own stream
+    current: a workspace dropped on return is then reused only by work ordered
+    after the kernels that read it."""
+    torch = _torch()
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _need(t, shape, dtype, name):
     if t is None:
         raise ValueError(f"{name} is required")
@@ -175,11 +205,14 @@ def _need(t, shape, dtype, name):
         raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
 
 
-def _workspace(params, T, dt, workspace, device):
-    torch = _torch()
-    need = ds4hc_workspace_bytes(params, T, dt)
+def _empty(shape, dtype, device):
+    return _torch().empty(shape, dtype=dtype, device=device)
+
+
+def _scratch(need, workspace, device):
+    """The caller's workspace, or a fresh one of `need` bytes (none if 0)."""
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = _empty(need, _torch().uint8, device)
     return workspace, (workspace.numel() * workspace.element_size() if workspace is not None else 0)
 
 
@@ -195,13 +228,14 @@ def ds4hc_pre(X, W, bias, *, rms_eps=1e-6, sinkhorn_iters=20, flags=0, layer_in=
     _need(X, (T, n, d), X.dtype, "X")
     _need(W, (m, n * d), torch.float16, "W")
     _need(bias, (m,), torch.float32, "bias")
-    if layer_in is None:
-        layer_in = torch.empty((T, d), dtype=X.dtype, device=X.device)
-    if coeffs is None:
-        coeffs = torch.empty((T, m), dtype=torch.float32, device=X.device)
-    if logits is None and want_logits:
-        logits = torch.empty((T, m), dtype=torch.float32, device=X.device)
-    workspace, ws_bytes = _workspace(p, T, dt, workspace, X.device)
+    with _on(stream):
+        if layer_in is None:
+            layer_in = _empty((T, d), X.dtype, X.device)
+        if coeffs is None:
+            coeffs = _empty((T, m), torch.float32, X.device)
+        if logits is None and want_logits:
+            logits = _empty((T, m), torch.float32, X.device)
+        workspace, ws_bytes = _scratch(ds4hc_workspace_bytes(p, T, dt), workspace, X.device)
     _check(ds4hc_pre_raw(p, T, dt, _ptr(X), _ptr(W), _ptr(bias), _ptr(layer_in), _ptr(coeffs),
                          _ptr(logits), _ptr(workspace), ws_bytes, _stream(stream)), "ds4hc_pre")
     return layer_in, coeffs, logits
@@ -220,13 +254,14 @@ def ds4hc_fused(X, W, bias, layer_out, *, rms_eps=1e-6, sinkhorn_iters=20, flags
     _need(W, (m, n * d), torch.float16, "W")
     _need(bias, (m,), torch.float32, "bias")
     _need(layer_out, (T, d), X.dtype, "layer_out")
-    if layer_in is None:
-        layer_in = torch.empty((T, d), dtype=X.dtype, device=X.device)
-    if coeffs is None and want_coeffs:
-        coeffs = torch.empty((T, m), dtype=torch.float32, device=X.device)
-    if X_out is None:
-        X_out = torch.empty_like(X)
-    workspace, ws_bytes = _workspace(p, T, dt, workspace, X.device)
+    with _on(stream):
+        if layer_in is None:
+            layer_in = _empty((T, d), X.dtype, X.device)
+        if coeffs is None and want_coeffs:
+            coeffs = _empty((T, m), torch.float32, X.device)
+        if X_out is None:
+            X_out = _empty(X.shape, X.dtype, X.device)
+        workspace, ws_bytes = _scratch(ds4hc_workspace_bytes(p, T, dt), workspace, X.device)
     _check(ds4hc_fused_raw(p, T, dt, _ptr(X), _ptr(W), _ptr(bias), _ptr(layer_out),
                            _ptr(layer_in), _ptr(coeffs), _ptr(X_out), _ptr(workspace), ws_bytes,
                            _stream(stream)), "ds4hc_fused")
@@ -244,8 +279,9 @@ def ds4hc_post(X, coeffs, layer_out, *, X_out=None, stream=None, rms_eps=1e-6,
     _need(X, (T, n, d), X.dtype, "X")
     _need(coeffs, (T, m), torch.float32, "coeffs")
     _need(layer_out, (T, d), X.dtype, "layer_out")
-    if X_out is None:
-        X_out = torch.empty_like(X)
+    with _on(stream):
+        if X_out is None:
+            X_out = _empty(X.shape, X.dtype, X.device)
     _check(ds4hc_post_raw(p, T, dt, _ptr(X), _ptr(coeffs), _ptr(layer_out), _ptr(X_out),
                           _stream(stream)), "ds4hc_post")
     return X_out
@@ -267,39 +303,22 @@ def ds4hc_post_pre(X, coeffs_prev, layer_out, W_next, bias_next, *, rms_eps=1e-6
     _need(layer_out, (T, d), X.dtype, "layer_out")
     _need(W_next, (m, n * d), torch.float16, "W_next")
     _need(bias_next, (m,), torch.float32, "bias_next")
-    if X_out is None:
-        X_out = torch.empty_like(X)
-    if layer_in is None:
-        layer_in = torch.empty((T, d), dtype=X.dtype, device=X.device)
-    if coeffs is None:
-        coeffs = torch.empty((T, m), dtype=torch.float32, device=X.device)
-    if logits is None and want_logits:
-        logits = torch.empty((T, m), dtype=torch.float32, device=X.device)
-    need = ds4hc_post_pre_workspace_bytes(p, T, dt)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with _on(stream):
+        if X_out is None:
+            X_out = _empty(X.shape, X.dtype, X.device)
+        if layer_in is None:
+            layer_in = _empty((T, d), X.dtype, X.device)
+        if coeffs is None:
+            coeffs = _empty((T, m), torch.float32, X.device)
+        if logits is None and want_logits:
+            logits = _empty((T, m), torch.float32, X.device)
+        workspace, ws_bytes = _scratch(ds4hc_post_pre_workspace_bytes(p, T, dt), workspace,
+                                       X.device)
     _check(ds4hc_post_pre_raw(p, T, dt, _ptr(X), _ptr(coeffs_prev), _ptr(layer_out), _ptr(W_next),
                               _ptr(bias_next), _ptr(X_out), _ptr(layer_in), _ptr(coeffs),
                               _ptr(logits), _ptr(workspace), ws_bytes, _stream(stream)),
            "ds4hc_post_pre")
     return X_out, layer_in, coeffs, logits
-
-
-def ds4hc_partials_workspace_bytes(params: Params, T: int, dtype: int) -> int:
-    return int(load().ds4hc_partials_workspace_bytes(ctypes.byref(params), int(T), int(dtype)))
-
-
-def ds4hc_partials_raw(params, T, dtype, X_share, W_share, partials, ws, ws_bytes, stream):
-    return load().ds4hc_partials(ctypes.byref(params), int(T), int(dtype), X_share, W_share,
-                                 partials, ws, int(ws_bytes), stream)
-
-
-def ds4hc_combine_raw(params, d_total, T, dtype, G, partials, bias, X_share, layer_out_share,
-                      layer_in_share, coeffs, X_out_share, stream):
-    return load().ds4hc_combine(ctypes.byref(params), int(d_total), int(T), int(dtype), int(G),
-                                partials, bias, X_share, layer_out_share, layer_in_share, coeffs,
-                                X_out_share, stream)
 
 
 def ds4hc_partials(X_share, W_share, *, flags=0, partials=None, workspace=None, stream=None):
@@ -312,12 +331,11 @@ def ds4hc_partials(X_share, W_share, *, flags=0, partials=None, workspace=None, 
     p = make_params(n, ds, 1e-6, 20, flags)
     _need(X_share, (T, n, ds), X_share.dtype, "X_share")
     _need(W_share, (m, n * ds), torch.float16, "W_share")
-    if partials is None:
-        partials = torch.empty((T, m + 1), dtype=torch.float32, device=X_share.device)
-    need = ds4hc_partials_workspace_bytes(p, T, dt)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=X_share.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with _on(stream):
+        if partials is None:
+            partials = _empty((T, m + 1), torch.float32, X_share.device)
+        workspace, ws_bytes = _scratch(ds4hc_partials_workspace_bytes(p, T, dt), workspace,
+                                       X_share.device)
     _check(ds4hc_partials_raw(p, T, dt, _ptr(X_share), _ptr(W_share), _ptr(partials),
                               _ptr(workspace), ws_bytes, _stream(stream)), "ds4hc_partials")
     return partials
@@ -337,12 +355,13 @@ def ds4hc_combine(partials, bias, X_share, layer_out_share, d_total, *, rms_eps=
     _need(bias, (m,), torch.float32, "bias")
     _need(X_share, (T, n, ds), X_share.dtype, "X_share")
     _need(layer_out_share, (T, ds), X_share.dtype, "layer_out_share")
-    if layer_in_share is None:
-        layer_in_share = torch.empty((T, ds), dtype=X_share.dtype, device=X_share.device)
-    if coeffs is None and want_coeffs:
-        coeffs = torch.empty((T, m), dtype=torch.float32, device=X_share.device)
-    if X_out_share is None:
-        X_out_share = torch.empty_like(X_share)
+    with _on(stream):
+        if layer_in_share is None:
+            layer_in_share = _empty((T, ds), X_share.dtype, X_share.device)
+        if coeffs is None and want_coeffs:
+            coeffs = _empty((T, m), torch.float32, X_share.device)
+        if X_out_share is None:
+            X_out_share = _empty(X_share.shape, X_share.dtype, X_share.device)
     _check(ds4hc_combine_raw(p, d_total, T, dt, G, _ptr(partials), _ptr(bias), _ptr(X_share),
                              _ptr(layer_out_share), _ptr(layer_in_share), _ptr(coeffs),
                              _ptr(X_out_share), _stream(stream)), "ds4hc_combine")
@@ -354,8 +373,9 @@ def ds4hc_sinkhorn(logits_res, *, iters=20, H=None, stream=None):
     torch = _torch()
     T, n, n2 = logits_res.shape
     _need(logits_res, (T, n, n), torch.float32, "logits_res")
-    if H is None:
-        H = torch.empty_like(logits_res)
+    with _on(stream):
+        if H is None:
+            H = _empty(logits_res.shape, torch.float32, logits_res.device)
     _check(ds4hc_sinkhorn_raw(T, n, iters, _ptr(logits_res), _ptr(H), _stream(stream)),
            "ds4hc_sinkhorn")
     return H

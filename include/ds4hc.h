@@ -31,9 +31,17 @@
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers on the calling thread's current
- *     HIP device, 16-byte aligned, dense row-major with the shapes given.
- *     The caller owns every buffer; the library allocates no device memory
- *     and keeps no mutable global state, so it is re-entrant and thread-safe.
+ *     HIP device, dense row-major with the shapes given. Alignment: the
+ *     state-typed arrays (X, X_out, layer_in, layer_out and their _share
+ *     forms) and W must be 16-byte aligned, since the kernels move them in
+ *     16-byte vectors; the float32 arrays (bias, coeffs, coeffs_prev, logits,
+ *     partials, logits_res, H) and the workspace need 4-byte alignment only.
+ *     A pointer that misses its alignment is DS4HC_ERR_INVALID_ARG.
+ *   - The caller owns every buffer; the library allocates no device memory.
+ *     Its only global state is a per-device cache of the compute-unit count
+ *     (looked up on a device's first call, read-only after, atomically
+ *     published) and a thread-local slot holding the last HIP error text, so
+ *     it is re-entrant and thread-safe.
  *   - Work is enqueued on `stream` (0 = the default stream) and the call
  *     returns without waiting. Faults during execution surface at the
  *     caller's next synchronisation of that stream.
@@ -93,7 +101,8 @@ typedef struct {
 /* Force one kernel path (all compute the same op; the default picks by T and
  * row length; forcing more than one is invalid):
  *   ROWRES  one token per workgroup, row kept in registers, VALU matvec;
- *   TILE    two tokens per workgroup, rows kept in registers, MFMA matvec;
+ *   TILE    persistent, one workgroup per CU striding over tiles of four
+ *           tokens, rows kept in registers, MFMA matvec;
  *   SPLITK  partials over K chunks into the workspace, then a combining kernel. */
 #define DS4HC_FLAG_FORCE_ROWRES 2u
 #define DS4HC_FLAG_FORCE_SPLITK 4u
@@ -152,7 +161,9 @@ ds4hc_status ds4hc_fused(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, co
                          size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes ds4hc_pre / ds4hc_fused need for these arguments (0 when
- * the chosen path needs none). Pure function; 0 for invalid arguments. */
+ * the chosen path needs none). Pure function; 0 for invalid arguments. It takes
+ * the state dtype because the split-K chunk width (64 lanes x one 16-byte
+ * vector) and hence the number of partial sums depend on it. */
 size_t ds4hc_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype);
 
 /*

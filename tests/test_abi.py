@@ -286,3 +286,52 @@ def test_partials_and_combine_validation():
     assert comb(li=f(2, 16)) == B.DS4HC_ERR_INVALID_ARG       # layer_in inside X_share
     assert comb(Xo=f(2, 16)) == B.DS4HC_ERR_INVALID_ARG       # shifted in-place
     assert comb(Xo=f(2)) == B.DS4HC_ERR_HIP                   # exact in place passes validation
+
+
+# ------------------------------------------------------------------ stated alignments
+
+@no_gpu_only
+@pytest.mark.parametrize("field,idx", [("bias", 2), ("coeffs", 5), ("ws", 7)])
+def test_fused_float_arrays_need_4_byte_alignment_only(field, idx):
+    """The float32 arrays and the workspace need 4-byte alignment: at a 4-byte
+    offset validation passes (so without a GPU the launch fails, ERR_HIP); at a
+    2-byte offset the call is rejected."""
+    p = B.make_params(4, 4096)
+    assert fused(p, 4, **{field: fake(idx, 4)}) == B.DS4HC_ERR_HIP
+    assert fused(p, 4, **{field: fake(idx, 2)}) == B.DS4HC_ERR_INVALID_ARG
+
+
+@no_gpu_only
+@pytest.mark.parametrize("field,idx", [("X", 0), ("W", 1), ("layer_out", 3), ("layer_in", 4),
+                                       ("X_out", 6)])
+def test_fused_state_arrays_and_weight_need_16_byte_alignment(field, idx):
+    p = B.make_params(4, 4096)
+    assert fused(p, 4, **{field: fake(idx, 8)}) == B.DS4HC_ERR_INVALID_ARG
+    assert fused(p, 4, **{field: fake(idx, 4)}) == B.DS4HC_ERR_INVALID_ARG
+
+
+@no_gpu_only
+def test_other_entry_points_float_arrays_need_4_byte_alignment_only():
+    p = B.make_params(4, 4096)
+    f = fake
+    # post_pre: coeffs_prev, bias_next, coeffs, logits, workspace at 4-byte offsets pass
+    assert post_pre(p, cp=f(1, 4), b=f(4, 4), c=f(7, 4), z=f(9, 4), ws=f(8, 4)) == B.DS4HC_ERR_HIP
+    assert post_pre(p, z=f(9, 2)) == B.DS4HC_ERR_INVALID_ARG
+    # pre: logits at a 4-byte offset passes
+    assert B.ds4hc_pre_raw(p, 4, 0, f(0), f(1), f(2, 4), f(3), f(4, 4), f(5, 4), f(7, 4), 1 << 30,
+                           None) == B.DS4HC_ERR_HIP
+    # post: coeffs at a 4-byte offset passes, X at 8 does not
+    assert B.ds4hc_post_raw(p, 4, 0, f(0), f(1, 4), f(2), f(3), None) == B.DS4HC_ERR_HIP
+    assert B.ds4hc_post_raw(p, 4, 0, f(0, 8), f(1), f(2), f(3), None) == B.DS4HC_ERR_INVALID_ARG
+    # sinkhorn: both arrays are float32
+    assert B.ds4hc_sinkhorn_raw(4, 4, 20, f(0, 4), f(1, 4), None) == B.DS4HC_ERR_HIP
+    assert B.ds4hc_sinkhorn_raw(4, 4, 20, f(0, 2), f(1), None) == B.DS4HC_ERR_INVALID_ARG
+    # partials: partials and workspace at 4-byte offsets pass, X_share at 8 does not
+    ps = B.make_params(4, 1024)
+    assert B.ds4hc_partials_raw(ps, 8, 0, f(0), f(1), f(2, 4), f(3, 4), 1 << 30, None) == B.DS4HC_ERR_HIP
+    assert B.ds4hc_partials_raw(ps, 8, 0, f(0, 8), f(1), f(2), f(3), 1 << 30, None) == B.DS4HC_ERR_INVALID_ARG
+    # combine: partials, bias, coeffs at 4-byte offsets pass, layer_in_share at 8 does not
+    assert B.ds4hc_combine_raw(ps, 4096, 8, 0, 4, f(0, 4), f(1, 4), f(2), f(3), f(4), f(5, 4), f(6),
+                               None) == B.DS4HC_ERR_HIP
+    assert B.ds4hc_combine_raw(ps, 4096, 8, 0, 4, f(0), f(1), f(2), f(3), f(4, 8), f(5), f(6),
+                               None) == B.DS4HC_ERR_INVALID_ARG

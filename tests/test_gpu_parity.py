@@ -1,10 +1,9 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
 the same seeded inputs, for every workload and both kernel paths.
 
-Small and reduced-T cases are compared on every output element; the
-full-size prefill and stress workloads, in the launch configuration the
-benchmark times, are compared on sampled token rows the oracle computes one
-by one (rows are independent).
+Every case is compared on every output element, the full-size prefill and
+stress workloads (in the launch configuration the benchmark times) included:
+there the oracle runs over token chunks, since rows are independent.
 """
 import numpy as np
 import pytest
@@ -171,43 +170,51 @@ def test_tile_prefill_recipe_several_tiles_in_place_and_pre():
     check_full(case, got, f"prefill T={T}/tile")
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled rows
+# ------------------------------------------------------------------ full-size workloads, every element
 
-def _sampled_check(case, flags, nsample, extra_rows=()):
+def _full_size_check(case, flags, chunk=1024):
+    """The workload at its full size, in the launch configuration the benchmark
+    times, compared with the oracle on every element of layer_in, X_out and the
+    coefficients. Rows are independent, so the oracle runs over token chunks and
+    its float64 outputs never hold more than `chunk` rows at a time."""
     torch = torch_mod()
-    got_li, got_c, got_xo = run_fused(case, flags)
-    rng = np.random.Generator(np.random.PCG64(123))
-    rows = np.unique(np.concatenate([[0, case.T - 1], rng.choice(case.T, nsample, replace=False),
-                                     np.asarray(extra_rows, dtype=np.int64)])).astype(np.int64)
-    rli, rc, rxo = oracle_fused(case, rows)
+    Xd, W, b, lo = case_to_device(case)
+    say(f"[gpu] ds4hc_fused full size {case.name} T={case.T} n={case.n} d={case.d} {case.dtype} "
+        f"flags={flags}: every element")
+    li, c, xo = B.ds4hc_fused(Xd, W, b, lo, rms_eps=case.eps, sinkhorn_iters=case.iters, flags=flags)
+    torch.cuda.synchronize()
+    del Xd, lo
     tol = TOL[case.dtype]
-    e1 = assert_close_rows(got_li[rows], rli, tol, f"{case.name} layer_in")
-    e2 = assert_close_rows(got_xo[rows], rxo, tol, f"{case.name} X_out")
-    e3 = assert_coeffs(got_c[rows], rc, f"{case.name} coeffs")
-    say(f"    {len(rows)} sampled rows: layer_in {e1:.2e}  X_out {e2:.2e}  coeffs {e3:.2e}")
-    # properties that hold for every row at any size
-    assert np.all(np.isfinite(got_xo)) and np.all(np.isfinite(got_li))
-    H = got_c[:, 2 * case.n:].reshape(case.T, case.n, case.n)
-    assert np.abs(H.sum(axis=1) - 1.0).max() < 1e-5      # columns normalised last
-    assert np.all((got_c >= 0) & (got_c <= 1))
-    del torch
-    return got_li, got_c, got_xo
+    got_c = c.cpu().numpy().astype(np.float64)
+    e = [0.0, 0.0, 0.0]
+    for a in range(0, case.T, chunk):
+        rows = slice(a, min(case.T, a + chunk))
+        rli, rc, rxo = oracle_fused(case, rows)
+        e[0] = max(e[0], assert_close_rows(torch_to_f64(li[rows]), rli, tol, f"{case.name} layer_in"))
+        e[1] = max(e[1], assert_close_rows(torch_to_f64(xo[rows]), rxo, tol, f"{case.name} X_out"))
+        e[2] = max(e[2], assert_coeffs(got_c[rows], rc, f"{case.name} coeffs"))
+    say(f"    all {case.T} rows: layer_in {e[0]:.2e}  X_out {e[1]:.2e}  coeffs {e[2]:.2e}")
+    assert np.all(np.isfinite(got_c)) and np.all((got_c >= 0) & (got_c <= 1))
+    return li, got_c, xo
 
 
-def test_prefill_full_size_sampled():
-    case = wl.make_prefill(0)
-    _sampled_check(case, 0, 96)
+def test_prefill_full_size_every_element():
+    _full_size_check(wl.make_prefill(0), 0)
 
 
-def test_stress_full_size_sampled():
+@pytest.mark.parametrize("path", ["default", "splitk"])
+def test_stress_full_size_every_element(path):
     case = wl.make_stress(0)
-    li, c, xo = _sampled_check(case, 0, 64, extra_rows=case.zero_rows[:16])
+    li, c, xo = _full_size_check(case, FLAGS[path])
     # every all-zero row: layer_in = 0, pre = post = 1/2, H = 1/n, X' = layer_out / 2 (bf16-exact)
+    torch = torch_mod()
     zr = case.zero_rows
-    assert np.all(li[zr] == 0.0)
+    zi = torch.from_numpy(zr).to(li.device)
+    assert np.all(torch_to_f64(li.index_select(0, zi)) == 0.0)
     assert np.all(c[zr, :8] == 0.5) and np.all(c[zr, 8:] == 0.25)
     lo = wl.state_to_f64(case.layer_out[zr], case.dtype)
-    np.testing.assert_array_equal(xo[zr], np.repeat(0.5 * lo[:, None, :], case.n, axis=1))
+    np.testing.assert_array_equal(torch_to_f64(xo.index_select(0, zi)),
+                                  np.repeat(0.5 * lo[:, None, :], case.n, axis=1))
 
 
 # ------------------------------------------------------------------ decode chain
@@ -243,7 +250,7 @@ def test_decode_chain_43_layers():
                     assert_close_rows(torch_to_f64(states[l + 1]), rx, TOL[wl.F32], f"layer {l} X'"))
         assert_coeffs(coeffs[l].cpu().numpy(), rc, f"layer {l} coeffs")
     ref = oracle.chain(wl.state_to_f64(case.X, case.dtype), case.chain_W, case.bias, case.chain_noise)
-    e2e = assert_close_rows(torch_to_f64(states[-1]), ref[-1], 1e-4, "chain end to end")
+    e2e = assert_close_rows(torch_to_f64(states[-1]), ref[-1], TOL[wl.F32], "chain end to end")
     say(f"    teacher-forced worst {worst:.2e}; end-to-end {e2e:.2e}")
 
 
@@ -338,27 +345,6 @@ def test_deterministic_repeats():
         for o in outs:
             h.update(o.view(torch.uint8).cpu().numpy().tobytes())
         digests.add(h.hexdigest())
-    assert len(digests) == 1
-
-
-@pytest.mark.parametrize("workload", ["prefill", "stress"])
-def test_deterministic_repeats_full_size(workload):
-    """The benchmark's own launch configuration (prefill: 4 tiles per tile-kernel
-    workgroup; stress: 16), run 3 times: every output identical bit for bit."""
-    import hashlib
-    torch = torch_mod()
-    case = wl.make_prefill(5) if workload == "prefill" else wl.make_stress(5)
-    X, W, b, lo = case_to_device(case)
-    say(f"[gpu] 3 repeats of ds4hc_fused, {workload} T={case.T} d={case.d} {case.dtype}")
-    digests = set()
-    for _ in range(3):
-        outs = B.ds4hc_fused(X, W, b, lo)
-        torch.cuda.synchronize()
-        h = hashlib.sha256()
-        for o in outs:
-            h.update(o.contiguous().view(torch.uint8).cpu().numpy().tobytes())
-        digests.add(h.hexdigest())
-        del outs
     assert len(digests) == 1
 
 
@@ -479,7 +465,7 @@ def test_decode_chain_43_layers_post_pre():
             X = B.ds4hc_post(X, c, lo)
     torch.cuda.synchronize()
     ref = oracle.chain(wl.state_to_f64(case.X, case.dtype), case.chain_W, case.bias, case.chain_noise)
-    e2e = assert_close_rows(torch_to_f64(X), ref[-1], 1e-4, "post_pre chain end to end")
+    e2e = assert_close_rows(torch_to_f64(X), ref[-1], TOL[wl.F32], "post_pre chain end to end")
     say(f"    end-to-end {e2e:.2e}")
 
 
@@ -519,3 +505,219 @@ def test_split_over_d(dtype, G, n, d, T):
     xo = torch.cat([o[2] for o in outs], dim=2)
     got = (torch_to_f64(li), outs[0][1].cpu().numpy().astype(np.float64), torch_to_f64(xo))
     check_full(case, got, f"split d G={G} T={T}")
+
+
+# ------------------------------------------------------------------ 86-site decode chain, eager and graph
+
+def _chain_86(torch, case, b, Ws, noise, states, ins, coeffs, ws, wsb):
+    """One decode token through the 86 HC sites (attention and FFN per layer of
+    43): HC-pre of site 0, then at every boundary the stand-in layer body
+    layer_out = 0.5 * layer_in + noise_s and one ds4hc_post_pre, and hc_post
+    after the last site. Every site's input state, layer_in and coefficients
+    land in buffers of their own (states[s], ins[s], coeffs[s]); raw calls on the
+    current stream with preallocated buffers, so the same code can be captured."""
+    import ctypes
+    P = ctypes.c_void_p
+    pt = lambda t: P(t.data_ptr())
+    sp = P(torch.cuda.current_stream().cuda_stream)
+    p = B.make_params(case.n, case.d)
+    sites = len(Ws)
+    st = B.ds4hc_pre_raw(p, 1, B.DS4HC_F32, pt(states[0]), pt(Ws[0]), pt(b), pt(ins[0]), pt(coeffs[0]),
+                         None, pt(ws), wsb, sp)
+    assert st == B.DS4HC_OK
+    lo = torch.empty((1, case.d), device="cuda")
+    for s_ in range(sites):
+        torch.add(noise[s_][None, :], ins[s_], alpha=0.5, out=lo)
+        if s_ + 1 < sites:
+            st = B.ds4hc_post_pre_raw(p, 1, B.DS4HC_F32, pt(states[s_]), pt(coeffs[s_]), pt(lo),
+                                      pt(Ws[s_ + 1]), pt(b), pt(states[s_ + 1]), pt(ins[s_ + 1]),
+                                      pt(coeffs[s_ + 1]), None, pt(ws), wsb, sp)
+        else:
+            st = B.ds4hc_post_raw(p, 1, B.DS4HC_F32, pt(states[s_]), pt(coeffs[s_]), pt(lo),
+                                  pt(states[s_ + 1]), sp)
+        assert st == B.DS4HC_OK
+
+
+def _check_chain_86(case, states, ins, coeffs, ref, what):
+    """Every site teacher forced (the oracle's HC-pre and hc_post fed the GPU's own
+    input state and layer_out) within 2e-5, and the end state against the
+    oracle's whole chain within 2e-5."""
+    worst = 0.0
+    for s_ in range(len(case.chain_W)):
+        Xs = torch_to_f64(states[s_])
+        rli, rc, _ = oracle.pre(Xs, case.chain_W[s_], case.bias)
+        worst = max(worst, assert_close_rows(torch_to_f64(ins[s_]), rli, TOL[wl.F32], f"{what} site {s_} layer_in"))
+        assert_coeffs(coeffs[s_].cpu().numpy(), rc, f"{what} site {s_} coeffs")
+        lo = torch_to_f64(ins[s_]) * 0.5 + case.chain_noise[s_].astype(np.float64)[None, :]
+        rx = oracle.post(Xs, rc, lo)
+        worst = max(worst, assert_close_rows(torch_to_f64(states[s_ + 1]), rx, TOL[wl.F32], f"{what} site {s_} X'"))
+    e2e = assert_close_rows(torch_to_f64(states[-1]), ref[-1], TOL[wl.F32], f"{what} end to end")
+    say(f"    {what}: teacher-forced worst {worst:.2e}; end-to-end {e2e:.2e} "
+        f"(state max |x| {np.abs(ref[-1]).max():.2e})")
+
+
+def test_decode_chain_86_sites_eager_and_graph():
+    """The decode token's 86 HC sites (the pages count 86 HC launches per decoded
+    token), T = 1, n = 4, d = 4096, float32, each site with its own f16 fn weight.
+    Run eagerly, then captured once as a HIP graph and replayed three times with
+    other eager work (the eager chain on other buffers) between the replays. The
+    eager run and every replay are checked against the oracle (per site and end
+    to end, 2e-5), and every replay is bitwise equal to the eager run."""
+    torch = torch_mod()
+    case = wl.make_chain(0, layers=86)
+    sites = len(case.chain_W)
+    b = torch.zeros(case.m, dtype=torch.float32, device="cuda")
+    Ws = [torch.from_numpy(w).cuda() for w in case.chain_W]
+    noise = torch.from_numpy(case.chain_noise).cuda()
+    p = B.make_params(case.n, case.d)
+    wsb = max(B.ds4hc_workspace_bytes(p, 1, B.DS4HC_F32), B.ds4hc_post_pre_workspace_bytes(p, 1, B.DS4HC_F32))
+
+    def buffers():
+        X0 = state_to_torch(case.X, case.dtype)
+        states = [X0] + [torch.empty_like(X0) for _ in range(sites)]
+        ins = [torch.empty((1, case.d), device="cuda") for _ in range(sites)]
+        coeffs = [torch.empty((1, case.m), device="cuda") for _ in range(sites)]
+        return states, ins, coeffs, torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    ref = oracle.chain(wl.state_to_f64(case.X, case.dtype), case.chain_W, case.bias, case.chain_noise)
+    say("[gpu] decode chain, 86 sites, eager")
+    eager = buffers()
+    _chain_86(torch, case, b, Ws, noise, *eager, wsb)
+    torch.cuda.synchronize()
+    _check_chain_86(case, *eager[:3], ref, "eager")
+
+    say("[gpu] decode chain, 86 sites, captured as one HIP graph")
+    gbuf = buffers()
+    other = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm the capture stream's allocations once
+        _chain_86(torch, case, b, Ws, noise, *gbuf, wsb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _chain_86(torch, case, b, Ws, noise, *gbuf, wsb)
+    for rep in range(3):
+        for t in gbuf[0][1:] + gbuf[1] + gbuf[2]:
+            t.fill_(float("nan"))      # a replay must rewrite every output
+        g.replay()
+        torch.cuda.synchronize()
+        for a, e in zip(gbuf[0] + gbuf[1] + gbuf[2], eager[0] + eager[1] + eager[2]):
+            assert torch.equal(a.view(torch.int32), e.view(torch.int32)), f"replay {rep} differs from eager"
+        _check_chain_86(case, *gbuf[:3], ref, f"graph replay {rep}")
+        _chain_86(torch, case, b, Ws, noise, *other, wsb)   # eager work between replays
+        torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ determinism: 20 repeats per workload
+
+def _bits(t):
+    import torch
+    t = t.contiguous()
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def _sha(ts):
+    import hashlib
+    h = hashlib.sha256()
+    for t in ts:
+        h.update(_bits(t).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+@pytest.mark.parametrize("workload", ["single", "verify", "prefill", "stress"])
+def test_deterministic_20_repeats(workload):
+    """The deterministic mode is bit-stable run to run: 20 runs of ds4hc_fused on
+    the same inputs, each followed by a call on other inputs of another size (so
+    the GPU's caches and workgroup placement differ between repeats), all
+    bitwise identical (compared on the GPU as integers, so NaN bits count too),
+    with the SHA-256 of the first and the last run's outputs equal."""
+    torch = torch_mod()
+    case = {"single": wl.make_single, "verify": wl.make_verify, "prefill": wl.make_prefill,
+            "stress": wl.make_stress}[workload](5)
+    X, W, b, lo = case_to_device(case)
+    noise_case = wl.make_random(99, 37, case.n, case.d, case.dtype)
+    Xn, Wn, bn, lon = case_to_device(noise_case)
+    say(f"[gpu] 20 repeats of ds4hc_fused, {workload} T={case.T} d={case.d} {case.dtype}, "
+        f"flags=DETERMINISTIC")
+    fl = B.DS4HC_FLAG_DETERMINISTIC
+    first = B.ds4hc_fused(X, W, b, lo, flags=fl)
+    torch.cuda.synchronize()
+    h0 = _sha(first)
+    for r in range(1, 20):
+        B.ds4hc_fused(Xn, Wn, bn, lon, flags=fl)
+        outs = B.ds4hc_fused(X, W, b, lo, flags=fl)
+        torch.cuda.synchronize()
+        for a, e in zip(outs, first):
+            assert torch.equal(_bits(a), _bits(e)), f"repeat {r} differs"
+        if r == 19:
+            assert _sha(outs) == h0
+        del outs
+    say(f"    sha256 {h0[:16]}... stable over 20 runs")
+
+
+def test_deterministic_20_repeats_chain():
+    """The 43-layer decode chain (ds4hc_pre, then one ds4hc_post_pre per layer
+    boundary, then ds4hc_post), 20 runs: every layer's layer_in and coefficients
+    and the end state bitwise identical run to run."""
+    torch = torch_mod()
+    case = wl.make_chain(5)
+    b = torch.zeros(case.m, dtype=torch.float32, device="cuda")
+    Ws = [torch.from_numpy(w).cuda() for w in case.chain_W]
+    noise = torch.from_numpy(case.chain_noise).cuda()
+    say("[gpu] 20 repeats of the 43-layer decode chain")
+
+    def run():
+        X = state_to_torch(case.X, case.dtype)
+        li, c, _ = B.ds4hc_pre(X, Ws[0], b)
+        outs = []
+        for l in range(len(Ws)):
+            outs += [li, c]
+            lo = li * 0.5 + noise[l][None, :]
+            if l + 1 < len(Ws):
+                X, li, c, _ = B.ds4hc_post_pre(X, c, lo, Ws[l + 1], b)
+            else:
+                X = B.ds4hc_post(X, c, lo)
+        torch.cuda.synchronize()
+        return outs + [X]
+
+    first = run()
+    h0 = _sha(first)
+    for r in range(1, 20):
+        outs = run()
+        for a, e in zip(outs, first):
+            assert torch.equal(_bits(a), _bits(e)), f"repeat {r} differs"
+    assert _sha(outs) == h0
+    say(f"    sha256 {h0[:16]}... stable over 20 runs")
+
+
+# ------------------------------------------------------------------ calls on a side stream
+
+def test_side_stream_matches_default_stream():
+    """The binding's stream= argument: ds4hc_fused (split-K, whose workspace the
+    binding allocates and drops) and ds4hc_post_pre at T = 1 enqueued on a side
+    stream, with the default stream kept busy meanwhile, give bitwise what the
+    same calls give on the default stream."""
+    torch = torch_mod()
+    case = wl.make_verify(21, T=1)
+    X, W, b, lo = case_to_device(case)
+    nxt = wl.make_random(1021, 1, case.n, case.d, case.dtype)
+    Wn = torch.from_numpy(nxt.W).cuda()
+    bn = torch.from_numpy(nxt.bias).cuda()
+    say("[gpu] ds4hc_fused / ds4hc_post_pre on a side stream, T=1")
+    ref_f = B.ds4hc_fused(X, W, b, lo)
+    ref_pp = B.ds4hc_post_pre(X, ref_f[1], lo, Wn, bn)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    big = torch.empty(1 << 26, device="cuda")
+    for rep in range(20):
+        got_f = B.ds4hc_fused(X, W, b, lo, stream=s)
+        got_pp = B.ds4hc_post_pre(X, got_f[1], lo, Wn, bn, stream=s)
+        big.fill_(float(rep))      # default-stream work that allocates meanwhile
+        junk = torch.empty(1 << 20, device="cuda").fill_(1.0)
+        torch.cuda.synchronize()
+        for a, e in zip(got_f + got_pp[:3], ref_f + ref_pp[:3]):
+            assert torch.equal(_bits(a), _bits(e)), f"side-stream repeat {rep} differs"
+        del junk
