@@ -27,7 +27,7 @@ DS4HC_FLAG_FORCE_SPLITK = 4
 DS4HC_FLAG_FORCE_TILE = 8
 
 EXPORTED = ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused", "ds4hc_workspace_bytes",
-            "ds4hc_post_pre", "ds4hc_post_pre_workspace_bytes",
+            "ds4hc_post_pre", "ds4hc_post_pre_workspace_bytes", "ds4hc_post_pre_noalloc",
             "ds4hc_partials", "ds4hc_partials_workspace_bytes", "ds4hc_combine",
             "ds4hc_status_string", "ds4hc_last_hip_error", "ds4hc_abi_version")
 
@@ -70,10 +70,11 @@ def load(path: str = LIB_PATH):
     lib.ds4hc_post.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp]
     lib.ds4hc_fused.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ds4hc_post_pre.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ds4hc_post_pre_noalloc.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ds4hc_partials.argtypes = [P, i64, ctypes.c_int, vp, vp, vp, vp, sz, vp]
     lib.ds4hc_combine.argtypes = [P, i32, i64, ctypes.c_int, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in ("ds4hc_pre", "ds4hc_sinkhorn", "ds4hc_post", "ds4hc_fused", "ds4hc_post_pre",
-              "ds4hc_partials", "ds4hc_combine"):
+              "ds4hc_post_pre_noalloc", "ds4hc_partials", "ds4hc_combine"):
         getattr(lib, f).restype = ctypes.c_int
     for f in ("ds4hc_workspace_bytes", "ds4hc_post_pre_workspace_bytes",
               "ds4hc_partials_workspace_bytes"):
@@ -119,6 +120,16 @@ def ds4hc_post_pre_raw(params, T, dtype, X, coeffs_prev, layer_out, W_next, bias
     return load().ds4hc_post_pre(ctypes.byref(params), int(T), int(dtype), X, coeffs_prev,
                                  layer_out, W_next, bias_next, X_out, layer_in, coeffs, logits, ws,
                                  int(ws_bytes), stream)
+
+
+NOALLOC_SCRATCH_BYTES = 2 << 20   # DS4HC_NOALLOC_SCRATCH_BYTES
+
+
+def ds4hc_post_pre_noalloc_raw(params, T, dtype, X, coeffs_prev, layer_out, W_next, bias_next,
+                               X_out, layer_in, coeffs, logits, stream):
+    return load().ds4hc_post_pre_noalloc(ctypes.byref(params), int(T), int(dtype), X, coeffs_prev,
+                                         layer_out, W_next, bias_next, X_out, layer_in, coeffs,
+                                         logits, stream)
 
 
 def ds4hc_pre_raw(params, T, dtype, X, W, bias, layer_in, coeffs, logits, ws, ws_bytes, stream):
@@ -379,3 +390,29 @@ def ds4hc_sinkhorn(logits_res, *, iters=20, H=None, stream=None):
     _check(ds4hc_sinkhorn_raw(T, n, iters, _ptr(logits_res), _ptr(H), _stream(stream)),
            "ds4hc_sinkhorn")
     return H
+
+
+def ds4hc_post_pre_noalloc(X, coeffs_prev, layer_out, W_next, bias_next, X_out, layer_in, coeffs,
+                           *, logits=None, rms_eps=1e-6, sinkhorn_iters=20, flags=0, stream=None):
+    """ds4hc_post_pre with the library's device-resident scratch instead of a
+    workspace. Every output is the caller's (this function allocates nothing)."""
+    torch = _torch()
+    T, n, d = X.shape
+    m = 2 * n + n * n
+    dt = _state_code(X)
+    p = make_params(n, d, rms_eps, sinkhorn_iters, flags)
+    _need(X, (T, n, d), X.dtype, "X")
+    _need(coeffs_prev, (T, m), torch.float32, "coeffs_prev")
+    _need(layer_out, (T, d), X.dtype, "layer_out")
+    _need(W_next, (m, n * d), torch.float16, "W_next")
+    _need(bias_next, (m,), torch.float32, "bias_next")
+    _need(X_out, (T, n, d), X.dtype, "X_out")
+    _need(layer_in, (T, d), X.dtype, "layer_in")
+    _need(coeffs, (T, m), torch.float32, "coeffs")
+    if logits is not None:
+        _need(logits, (T, m), torch.float32, "logits")
+    _check(ds4hc_post_pre_noalloc_raw(p, T, dt, _ptr(X), _ptr(coeffs_prev), _ptr(layer_out),
+                                      _ptr(W_next), _ptr(bias_next), _ptr(X_out), _ptr(layer_in),
+                                      _ptr(coeffs), _ptr(logits), _stream(stream)),
+           "ds4hc_post_pre_noalloc")
+    return X_out, layer_in, coeffs, logits

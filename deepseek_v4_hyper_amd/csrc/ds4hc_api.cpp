@@ -2,11 +2,13 @@
 // validation, choice between the row-resident and split-K paths, and launch.
 //
 // Nothing here touches the GPU until every argument has been checked, so all
-// rejections are free of side effects. The library holds no device memory:
-// per-device scratch is the caller's workspace argument. (lucebox PR #507
-// "correct layer-split HC handoff and per-device state" fixed a bug where an
-// HC scratch buffer was shared across devices; a library without global
-// scratch cannot have it.)
+// rejections are free of side effects. The library allocates no device memory:
+// per-device scratch is the caller's workspace argument, except for
+// ds4hc_post_pre_noalloc, whose scratch is a fixed device array with one copy
+// per device. (lucebox PR #507 "correct layer-split HC handoff and per-device
+// state" fixed a bug where an HC scratch buffer was shared across devices;
+// scratch that is the caller's, or a device-resident array looked up per
+// device, cannot have it.)
 #include "ds4hc.h"
 
 #include <math.h>
@@ -199,15 +201,14 @@ ds4hc_status make_post_pre_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt
     return DS4HC_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-ds4hc_status ds4hc_post_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
-                            const float *coeffs_prev, const void *layer_out,
-                            const uint16_t *W_f16_next, const float *bias_next, void *X_out,
-                            void *layer_in, float *coeffs, float *logits_opt, void *workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+// ds4hc_post_pre and its variant that allocates nothing: the same validation,
+// plan and kernels; with `noalloc` the workspace is the library's device-resident
+// scratch array instead of the caller's buffer.
+ds4hc_status post_pre_impl(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                           const float *coeffs_prev, const void *layer_out,
+                           const uint16_t *W_f16_next, const float *bias_next, void *X_out,
+                           void *layer_in, float *coeffs, float *logits_opt, void *workspace,
+                           size_t workspace_bytes, bool noalloc, hipStream_t stream) {
     ds4hc_status st = check_params(p, T, dtype);
     if (st != DS4HC_OK || T == 0) return st;
     if (!X || !coeffs_prev || !layer_out || !W_f16_next || !bias_next || !X_out || !layer_in ||
@@ -221,7 +222,14 @@ ds4hc_status ds4hc_post_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype,
     PostPrePlan pp;
     st = make_post_pre_plan(p, T, dtype, &pp);
     if (st != DS4HC_OK) return st;
-    if (pp.ws_bytes > 0 && (!workspace || workspace_bytes < pp.ws_bytes)) return DS4HC_ERR_INVALID_ARG;
+    if (noalloc) {
+        // the static array has a fixed size: larger needs are refused, not allocated
+        if (pp.ws_bytes > ds4hc::NOALLOC_SCRATCH_BYTES) return DS4HC_ERR_UNSUPPORTED;
+        workspace = nullptr;
+        workspace_bytes = 0;
+    } else if (pp.ws_bytes > 0 && (!workspace || workspace_bytes < pp.ws_bytes)) {
+        return DS4HC_ERR_INVALID_ARG;
+    }
 
     const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
     const uint64_t sb = (uint64_t)state_bytes(dtype), K = (uint64_t)n * d, uT = (uint64_t)T;
@@ -239,10 +247,38 @@ ds4hc_status ds4hc_post_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype,
             if (!in_place && overlap(all[a], all[b])) return DS4HC_ERR_INVALID_ARG;
         }
     }
+    if (noalloc && pp.ws_bytes > 0) {
+        // every argument is valid: now the device address of the scratch array
+        // (a symbol lookup on the device's first call, no allocation)
+        const hipError_t e = ds4hc::noalloc_scratch(&workspace);
+        if (e != hipSuccess) return hip_fail(e);
+    }
     ds4hc::FusedArgs a{n, d, (int)dtype, p->sinkhorn_iters, T, p->rms_eps, X, W_f16_next, bias_next,
                        layer_out, layer_in, coeffs, logits_opt, X_out, static_cast<float *>(workspace)};
     const hipError_t e = ds4hc::launch_post_pre(a, coeffs_prev, pp.one_pass, pp.pre.path, stream);
     return e == hipSuccess ? DS4HC_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+ds4hc_status ds4hc_post_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X,
+                            const float *coeffs_prev, const void *layer_out,
+                            const uint16_t *W_f16_next, const float *bias_next, void *X_out,
+                            void *layer_in, float *coeffs, float *logits_opt, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    return post_pre_impl(p, T, dtype, X, coeffs_prev, layer_out, W_f16_next, bias_next, X_out,
+                         layer_in, coeffs, logits_opt, workspace, workspace_bytes, false, stream);
+}
+
+ds4hc_status ds4hc_post_pre_noalloc(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype,
+                                    const void *X, const float *coeffs_prev, const void *layer_out,
+                                    const uint16_t *W_f16_next, const float *bias_next,
+                                    void *X_out, void *layer_in, float *coeffs, float *logits_opt,
+                                    hipStream_t stream) {
+    return post_pre_impl(p, T, dtype, X, coeffs_prev, layer_out, W_f16_next, bias_next, X_out,
+                         layer_in, coeffs, logits_opt, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -1332,6 +1332,31 @@ static hipError_t device_cu_count(int *cus) {
     return hipSuccess;
 }
 
+// Scratch of the entry point that allocates nothing (ds4hc_post_pre_noalloc):
+// a file-scope device array, one copy on every device the library runs on,
+// held until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: kernels and copies get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void **ptr) {
+    static std::atomic<void *> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void *p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        cache[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 template <int N, int DT, int MODE>
 static hipError_t launch_tile_n(int cs, const FusedArgs &a, hipStream_t s) {
     // Persistent: one workgroup per compute unit (the weight ring takes most

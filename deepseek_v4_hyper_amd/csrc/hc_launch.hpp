@@ -49,6 +49,10 @@ hipError_t launch_partials(const FusedArgs &a, int path, hipStream_t s);
 hipError_t launch_combine(const FusedArgs &a, int d_total, int G, const float *partials,
                           hipStream_t s);
 int post_pre_chunks(int d, int dt);
+// Bytes of the device-resident scratch array behind ds4hc_post_pre_noalloc,
+// and its address on the current device (looked up once per device).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(2) << 20;
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_post_pre(const FusedArgs &a, const float *coeffs_prev, bool one_pass, int path,
                            hipStream_t s);
 

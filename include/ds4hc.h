@@ -40,8 +40,10 @@
  *   - The caller owns every buffer; the library allocates no device memory.
  *     Its only global state is a per-device cache of the compute-unit count
  *     (looked up on a device's first call, read-only after, atomically
- *     published) and a thread-local slot holding the last HIP error text, so
- *     it is re-entrant and thread-safe.
+ *     published), a thread-local slot holding the last HIP error text, and
+ *     the fixed scratch array of ds4hc_post_pre_noalloc (below) with its
+ *     per-device address cache. Every other entry point is re-entrant and
+ *     thread-safe.
  *   - Work is enqueued on `stream` (0 = the default stream) and the call
  *     returns without waiting. Faults during execution surface at the
  *     caller's next synchronisation of that stream.
@@ -198,6 +200,31 @@ ds4hc_status ds4hc_post_pre(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype,
 
 /* Workspace bytes ds4hc_post_pre needs for these arguments (0 if none or invalid). */
 size_t ds4hc_post_pre_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype);
+
+/*
+ * ds4hc_post_pre_noalloc -- ds4hc_post_pre for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments, semantics, kernels and results (bit
+ * for bit) as ds4hc_post_pre, without the workspace: the split-K partial sums
+ * go to a file-scope device array of DS4HC_NOALLOC_SCRATCH_BYTES bytes that
+ * every device the library runs on holds until the process ends. The call
+ * allocates nothing; on a device's first call it looks up the array's device
+ * address (hipGetSymbolAddress) and keeps it.
+ * Limit: a call whose ds4hc_post_pre_workspace_bytes(p, T, dtype) exceeds
+ * DS4HC_NOALLOC_SCRATCH_BYTES returns DS4HC_ERR_UNSUPPORTED and enqueues
+ * nothing (n = 4: T * ceil(d / (32 * V)) * 100 bytes, V = 4 for float32 and 8
+ * for bfloat16 state; d = 4096 float32 fits every T of the one-pass path).
+ * All calls on one device share that device's array, and the kernels
+ * overwrite every byte they read before reading it (nothing must start at
+ * zero). Calls that overlap on one device race on the array: order them on
+ * one stream.
+ */
+#define DS4HC_NOALLOC_SCRATCH_BYTES (2u << 20)
+ds4hc_status ds4hc_post_pre_noalloc(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype,
+                                    const void *X, const float *coeffs_prev, const void *layer_out,
+                                    const uint16_t *W_f16_next, const float *bias_next,
+                                    void *X_out, void *layer_in, float *coeffs, float *logits_opt,
+                                    hipStream_t stream);
 
 /*
  * Split over d (one GPU's share of the columns of every stream; the exchange

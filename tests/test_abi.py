@@ -335,3 +335,35 @@ def test_other_entry_points_float_arrays_need_4_byte_alignment_only():
                                None) == B.DS4HC_ERR_HIP
     assert B.ds4hc_combine_raw(ps, 4096, 8, 0, 4, f(0), f(1), f(2), f(3), f(4, 8), f(5), f(6),
                                None) == B.DS4HC_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ the entry point that allocates nothing
+
+@no_gpu_only
+def test_post_pre_noalloc_validation():
+    """Rejections happen on the host before any HIP call: bad arguments, and a
+    workspace need beyond the fixed scratch array (DS4HC_ERR_UNSUPPORTED)."""
+    f = fake
+
+    def call(p, T=8, **over):
+        a = dict(X=f(0), cp=f(1), lo=f(2), W=f(3), b=f(4), X_out=f(5), li=f(6), c=f(7), z=None)
+        a.update(over)
+        return B.ds4hc_post_pre_noalloc_raw(p, T, 0, a["X"], a["cp"], a["lo"], a["W"], a["b"],
+                                            a["X_out"], a["li"], a["c"], a["z"], None)
+    p = B.make_params(4, 4096)
+    assert call(p, X=None) == B.DS4HC_ERR_INVALID_ARG
+    assert call(p, X_out=f(0, 16)) == B.DS4HC_ERR_INVALID_ARG
+    assert call(p, c=f(1)) == B.DS4HC_ERR_INVALID_ARG
+    assert call(p, 0, X=None, cp=None, lo=None, W=None, b=None, X_out=None, li=None, c=None) == B.DS4HC_OK
+    pf = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_SPLITK)
+    assert B.ds4hc_post_pre_workspace_bytes(pf, 4096, B.DS4HC_F32) > B.NOALLOC_SCRATCH_BYTES
+    assert call(pf, 4096) == B.DS4HC_ERR_UNSUPPORTED
+    # within the scratch: validation passes, so without a GPU the device lookup fails (ERR_HIP)
+    assert B.ds4hc_post_pre_workspace_bytes(p, 160, B.DS4HC_F32) <= B.NOALLOC_SCRATCH_BYTES
+    assert call(p, 160) == B.DS4HC_ERR_HIP
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "ds4hc.h")).read()
+    m = re.search(r"#define DS4HC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
