@@ -321,11 +321,28 @@ def split_share(G, steps, warmup):
     li = torch.empty((T, ds), device="cuda")
     cf = torch.empty((T, m), device="cuda")
     xo = torch.empty_like(Xs)
+    # raw C-ABI calls on preallocated buffers: the binding's per-call checks in
+    # Python would otherwise set the pace of these ~10-30 us kernels
+    ps = B.make_params(n, ds)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    pt = lambda t: ctypes.c_void_p(t.data_ptr())
+    wsb = B.ds4hc_partials_workspace_bytes(ps, T, B.DS4HC_F32)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    a_part = (pt(Xs), pt(Ws), pt(P[0]), pt(ws))
+    a_comb = (pt(P), pt(b), pt(Xs), pt(los), pt(li), pt(cf), pt(xo))
+
+    def part():
+        st = B.ds4hc_partials_raw(ps, T, B.DS4HC_F32, a_part[0], a_part[1], a_part[2], a_part[3], wsb, sp)
+        if st != B.DS4HC_OK:
+            raise B.Ds4hcError(st, "ds4hc_partials")
+
+    def comb():
+        st = B.ds4hc_combine_raw(ps, d, T, B.DS4HC_F32, G, *a_comb, sp)
+        if st != B.DS4HC_OK:
+            raise B.Ds4hcError(st, "ds4hc_combine")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     res = {}
-    for name, fn in (("partials", lambda: B.ds4hc_partials(Xs, Ws, partials=P[0])),
-                     ("combine", lambda: B.ds4hc_combine(P, b, Xs, los, d, coeffs=cf, layer_in_share=li,
-                                                         X_out_share=xo))):
+    for name, fn in (("partials", part), ("combine", comb)):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
