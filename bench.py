@@ -11,8 +11,8 @@ Prints one JSON line. Three input sets are rotated so no step starts with its
 inputs warm in the 256 MiB last-level cache. Before the warm-up steps the op
 runs for ~100 ms of wall time, so the timed steps see steady clocks however
 few warm-up steps are asked for. Besides the headline figures the line holds:
-the bandwidth of a plain 1 GiB device copy measured in the same process (and
-the op's fraction of it), the per-call latency of the decode-sized workloads
+the bandwidth of a plain 1 GiB device copy (libds4hc_bw.so) measured in the
+same process, and the op's fraction of it, the per-call latency of the decode-sized workloads
 (T=1, d=256 and T=4, d=4096) warm and with the caches flushed, and the CPU
 baseline: the fp64 oracle on the same workload with all host cores, and with
 one thread on a sample of it.
@@ -145,21 +145,35 @@ def cpu_baseline(case, min_runs=3, min_seconds=5.0, max_runs=50, single_tokens=1
 
 
 def copy_bandwidth(nbytes=1 << 30, reps=20):
-    """Plain device copy (torch's elementwise copy kernel, read nbytes + write
-    nbytes) at steady clocks: GB/s of read + write bytes, median over reps."""
+    """A plain device copy at steady clocks (libds4hc_bw.so: 16-byte
+    non-temporal loads and stores, 1 GiB): GB/s of read + write bytes, median
+    over reps. The achievable bandwidth of a streaming kernel on this GPU."""
     import torch
+    from deepseek_v4_hyper_amd import build_lib
+    lib = ctypes.CDLL(build_lib.LIB_BW)
+    lib.ds4hc_bw_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.ds4hc_bw_copy.restype = ctypes.c_int
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def copy():
+        rc = lib.ds4hc_bw_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), nbytes, sp)
+        if rc != 0:
+            raise RuntimeError(f"ds4hc_bw_copy failed: {rc}")
     for _ in range(3):
-        b.copy_(a)
+        copy()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     for s, e in ev:
-        s.record()
-        b.copy_(a)
-        e.record()
+        s.record(stream)
+        copy()
+        e.record(stream)
     torch.cuda.synchronize()
+    if not torch.equal(a[:1024], b[:1024]) or not torch.equal(a[-1024:], b[-1024:]):
+        raise RuntimeError("ds4hc_bw_copy: the copy is wrong")
     ms = float(np.median([s.elapsed_time(e) for s, e in ev]))
     del a, b
     return 2 * nbytes / (ms * 1e-3) / 1e9

@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libds4hc.so")
 SOURCES = ["hc_kernels.hip", "ds4hc_api.cpp"]
+# the plain device copy bench.py measures beside the op (not part of the op's ABI)
+LIB_BW = os.path.join(PKG, "libds4hc_bw.so")
+SOURCES_BW = ["bw_copy.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -43,12 +46,18 @@ def _stale(obj: str) -> bool:
 
 
 def build(verbose: bool = False, incremental: bool = False) -> str:
-    """Compile every source and link the shared library. Returns its path.
+    """Compile every source and link the shared libraries (the op's and the copy
+    bench.py measures beside it). Returns the op library's path.
     With incremental=True, objects newer than every source and header are reused."""
+    _link(SOURCES_BW, LIB_BW, verbose, incremental)
+    return _link(SOURCES, LIB, verbose, incremental)
+
+
+def _link(sources, lib, verbose, incremental):
     objs = []
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    for src in source_paths():
+    for src in [os.path.join(CSRC, s) for s in sources]:
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
         objs.append(obj)
         if incremental and not _stale(obj):
@@ -58,13 +67,13 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
