@@ -1054,63 +1054,77 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
     const size_t K = (size_t)N * d;
     const int c0 = (blockIdx.y * POSTPRE_LANES + cl) * V;
     const bool ok = c0 < d;
+    const int cs = ok ? c0 : 0;                // in-bounds column for every lane
     const int tbase = blockIdx.x * SPLITK_TOKENS;
+
+    // The next site's weights for this lane's rows and columns, loaded once for
+    // all tokens of the group and first of all: they do not depend on the post
+    // update, so their round trip overlaps that of the state and the previous
+    // coefficients instead of following it (T = 1, d = 4096: the kernel's
+    // weight loads used to be issued only after the post update, itself after
+    // four dependent loads of the coefficients). Rows past M (last group when 4
+    // does not divide M) read row M - 1 and are never stored; lanes past d read
+    // column 0 and use zero weights.
+    HalfVec<V> w[N][RPW];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int j = min(row0 + r, M - 1);
+            w[i][r] = load_half_vec<V>(W + (size_t)j * K + (size_t)i * d + cs);
+            if (!ok) w[i][r].raw = {};
+        }
 
 #pragma unroll
     for (int tt = 0; tt < SPLITK_TOKENS; ++tt) {
         const int t = tbase + tt;
         if (t >= T) break;  // uniform across the wavefront
-        const float *cp = coeffs_prev + (size_t)t * M;
+        // the previous site's coefficients, the state and layer_out: all loads
+        // issued together, before the first store
+        float cp[M];
+#pragma unroll
+        for (int j = 0; j < M; ++j) cp[j] = coeffs_prev[(size_t)t * M + j];
+        StateVec<DT> xin[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) xin[i] = load_vec<DT>(X, (size_t)t * K + (size_t)i * d + cs);
+        const StateVec<DT> lv = load_vec<DT>(layer_out, (size_t)t * d + cs);
         float x[N][V];
         float acc[RPW + 1];
 #pragma unroll
         for (int j = 0; j <= RPW; ++j) acc[j] = 0.f;
-        if (ok) {
-            float xin[N][V];
 #pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const StateVec<DT> v = load_vec<DT>(X, (size_t)t * K + (size_t)i * d + c0);
+        for (int i = 0; i < N; ++i) {
+            float o[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e) xin[i][e] = vec_get<DT>(v, e);
+            for (int e = 0; e < V; ++e) {
+                float s = cp[2 * N + i * N] * vec_get<DT>(xin[0], e);
+#pragma unroll
+                for (int j = 1; j < N; ++j) s = fmaf(cp[2 * N + i * N + j], vec_get<DT>(xin[j], e), s);
+                o[e] = fmaf(cp[N + i], vec_get<DT>(lv, e), s);
             }
-            const StateVec<DT> lv = load_vec<DT>(layer_out, (size_t)t * d + c0);
+            // (the row groups read X in the same instruction: group 0's
+            // store cannot overtake another group's load)
+            if (ok && grp == 0) store_vec<DT>(X_out, (size_t)t * K + (size_t)i * d + c0, o);
+            // the next site sees X' as stored (rounded to the state type);
+            // lanes past d contribute zeros
 #pragma unroll
-            for (int i = 0; i < N; ++i) {
-                float o[V];
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    float s = cp[2 * N + i * N] * xin[0][e];
-#pragma unroll
-                    for (int j = 1; j < N; ++j) s = fmaf(cp[2 * N + i * N + j], xin[j][e], s);
-                    o[e] = fmaf(cp[N + i], vec_get<DT>(lv, e), s);
-                }
-                // (the row groups read X in the same instruction: group 0's
-                // store cannot overtake another group's load)
-                if (grp == 0) store_vec<DT>(X_out, (size_t)t * K + (size_t)i * d + c0, o);
-                // the next site sees X' as stored (rounded to the state type)
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    if constexpr (DT == DT_F32)
-                        x[i][e] = o[e];
-                    else
-                        x[i][e] = bf16_lo(f32_to_bf16_bits(o[e]));
-                }
+            for (int e = 0; e < V; ++e) {
+                float v;
+                if constexpr (DT == DT_F32)
+                    v = o[e];
+                else
+                    v = bf16_lo(f32_to_bf16_bits(o[e]));
+                x[i][e] = ok ? v : 0.f;
             }
+        }
 #pragma unroll
-            for (int i = 0; i < N; ++i) {
+        for (int i = 0; i < N; ++i) {
 #pragma unroll
-                for (int r = 0; r < RPW; ++r) {
-                    // rows past M (last group when 4 does not divide M) read
-                    // row M - 1 and are never stored: no branch around the
-                    // loads, so they all stay in flight together
-                    const int j = min(row0 + r, M - 1);
-                    const HalfVec<V> w = load_half_vec<V>(W + (size_t)j * K + (size_t)i * d + c0);
+            for (int r = 0; r < RPW; ++r)
 #pragma unroll
-                    for (int e = 0; e < V; ++e) acc[r] = fmaf(half_get<V>(w, e), x[i][e], acc[r]);
-                }
+                for (int e = 0; e < V; ++e) acc[r] = fmaf(half_get<V>(w[i][r], e), x[i][e], acc[r]);
 #pragma unroll
-                for (int e = 0; e < V; ++e) acc[RPW] = fmaf(x[i][e], x[i][e], acc[RPW]);
-            }
+            for (int e = 0; e < V; ++e) acc[RPW] = fmaf(x[i][e], x[i][e], acc[RPW]);
         }
 #pragma unroll
         for (int j = 0; j <= RPW; ++j) acc[j] = chunk_sum(acc[j]);
