@@ -933,6 +933,37 @@ __global__ __launch_bounds__(TILE_THREADS, 1) void hc_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Sum of p[c * stride] over chunks c = 0 .. P-1, added in ascending c, with PB
+// loads in flight at a time. A last batch shorter than PB reads the final chunk
+// again in its unused slots (every load is in bounds and none waits on
+// another) and skips those slots in the sum. Loading the remainder one chunk
+// at a time instead serialised it: 28 chunks at d = 7168 bf16 were 28
+// dependent trips past L2.
+// ---------------------------------------------------------------------------
+template <int PB>
+__device__ __forceinline__ float sum_chunks(const float *__restrict__ p, size_t stride, int P) {
+    float tot = 0.f;
+    int c = 0;
+    for (; c + PB <= P; c += PB) {
+        float v[PB];
+#pragma unroll
+        for (int k = 0; k < PB; ++k) v[k] = p[(size_t)(c + k) * stride];
+#pragma unroll
+        for (int k = 0; k < PB; ++k) tot += v[k];
+    }
+    if (c < P) {
+        const int last = P - 1 - c;  // < PB
+        float v[PB];
+#pragma unroll
+        for (int k = 0; k < PB; ++k) v[k] = p[(size_t)(c + min(k, last)) * stride];
+#pragma unroll
+        for (int k = 0; k < PB; ++k)
+            if (k <= last) tot += v[k];
+    }
+    return tot;
+}
+
+// ---------------------------------------------------------------------------
 // Split-K partials: grid (ceil(T / SPLITK_TOKENS), P chunks), one wavefront.
 // Chunk p covers flattened columns [p*64*V, (p+1)*64*V) of K; lane l owns V
 // consecutive columns. Writes ws[p][t][0..M) = partial dots, ws[p][t][M] =
@@ -998,61 +1029,61 @@ __global__ __launch_bounds__(64) void hc_chunk_sum_kernel(int T, int P, const fl
     const int lane = threadIdx.x;
     const size_t t = blockIdx.x;
     if (lane > M) return;
-    const float *p = ws + t * (M + 1) + lane;
-    const size_t stride = (size_t)T * (M + 1);
-    float tot = 0.f;
-    for (int c = 0; c < P; ++c) tot += p[(size_t)c * stride];
-    out[t * (M + 1) + lane] = tot;
+    out[t * (M + 1) + lane] = sum_chunks<32>(ws + t * (M + 1) + lane, (size_t)T * (M + 1), P);
 }
 
 // ---------------------------------------------------------------------------
 // One-pass chain step, split-K part: grid (ceil(T / SPLITK_TOKENS), P2), one
-// wavefront. Chunk p covers columns [p*32*V, (p+1)*32*V) of every stream: lane
-// l = 32 g + c holds the V columns p*32*V + c*V .. of all n streams, so it can
-// apply the previous site's post update X' = H.X + post (x) layer_out itself
-// (same operation order as hc_post_kernel, so X' is bitwise what ds4hc_post
-// writes); the two 32-lane groups g hold the same columns and split the M fn
-// rows of the next site (rows g*RPW ..), and group 0 stores X'. At decode sizes
-// the step is bound by each CU's weight stream: chunks of 32 lanes spread W
-// over twice as many CUs as chunks of 64 (6.2 against 7.5 us at T = 1,
-// d = 4096, fp32), while 16-lane chunks, with 8-byte W loads per lane and X
-// read by four groups, take 9.1 us. Writes the partial dots of the next site's
-// fn projection and the partial sum of squares of X' (as rounded to the state
-// type) to ws[p][t][0..M].
+// wavefront. With L lanes per column chunk (16 or 32), chunk p covers columns
+// [p*L*V, (p+1)*L*V) of every stream: lane l = L g + c holds the V columns
+// p*L*V + c*V .. of all n streams, so it can apply the previous site's post
+// update X' = H.X + post (x) layer_out itself (same operation order as
+// hc_post_kernel, so X' is bitwise what ds4hc_post writes); the 64 / L lane
+// groups g hold the same columns and split the M fn rows of the next site
+// (rows g*RPW ..), and group 0 stores X'. Writes the partial dots of the next
+// site's fn projection and the partial sum of squares of X' (as rounded to the
+// state type) to ws[p][t][0..M].
+//
+// At decode sizes the step is latency-bound: narrower chunks spread W over
+// more CUs and give each lane fewer loads, but add partials for the finish
+// kernel to combine. post_pre_lanes() takes 16 lanes while that gives at most
+// 64 chunks, else 32. Graph-replayed ds4hc_post_pre at T = 1, 16 against 32
+// lanes: d = 4096 fp32 6.2 / 6.7 us, d = 7168 bf16 8.0 / 8.3 us, d = 7168 fp32
+// (112 chunks at 16 lanes) 8.0 / 7.7 us.
 // ---------------------------------------------------------------------------
-constexpr int POSTPRE_LANES = 32;  // lanes per column chunk; two row groups per wave
 
-// Sum over the POSTPRE_LANES lanes of a column chunk (every lane gets the
-// total): within each 16-lane DPP row, then across row pairs by the gfx950 row
-// swap when a chunk spans two rows.
+// Sum over the L lanes of a column chunk (every lane gets the total): within
+// each 16-lane DPP row, then across row pairs by the gfx950 row swap when a
+// chunk spans two rows.
+template <int L>
 __device__ __forceinline__ float chunk_sum(float v) {
-    static_assert(POSTPRE_LANES == 16 || POSTPRE_LANES == 32, "chunk of one or two DPP rows");
+    static_assert(L == 16 || L == 32, "chunk of one or two DPP rows");
     v += dpp_mov<0x128>(v);  // row_ror:8
     v += dpp_mov<0x124>(v);  // row_ror:4
     v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
     v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-    if constexpr (POSTPRE_LANES == 32) {
+    if constexpr (L == 32) {
         const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
         v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
     }
     return v;
 }
 
-template <int N, int DT>
+template <int N, int DT, int L>
 __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
     int d, int T, const void *__restrict__ X, const float *__restrict__ coeffs_prev,
     const void *__restrict__ layer_out, const uint16_t *__restrict__ W, void *X_out,
     float *__restrict__ ws) {
     constexpr int V = StateVec<DT>::V;
     constexpr int M = n_logits(N);
-    constexpr int RG = 64 / POSTPRE_LANES;     // row groups
+    constexpr int RG = 64 / L;                 // row groups
     constexpr int RPW = (M + RG - 1) / RG;     // fn rows per group
     const int lane = threadIdx.x;
-    const int grp = lane / POSTPRE_LANES, cl = lane % POSTPRE_LANES;
+    const int grp = lane / L, cl = lane % L;
     const int row0 = grp * RPW;
     const bool ss_group = grp == RG - 1;
     const size_t K = (size_t)N * d;
-    const int c0 = (blockIdx.y * POSTPRE_LANES + cl) * V;
+    const int c0 = (blockIdx.y * L + cl) * V;
     const bool ok = c0 < d;
     const int cs = ok ? c0 : 0;                // in-bounds column for every lane
     const int tbase = blockIdx.x * SPLITK_TOKENS;
@@ -1127,7 +1158,7 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
             for (int e = 0; e < V; ++e) acc[RPW] = fmaf(x[i][e], x[i][e], acc[RPW]);
         }
 #pragma unroll
-        for (int j = 0; j <= RPW; ++j) acc[j] = chunk_sum(acc[j]);
+        for (int j = 0; j <= RPW; ++j) acc[j] = chunk_sum<L>(acc[j]);
         float *out = ws + ((size_t)blockIdx.y * T + t) * (M + 1);
         if (cl < RPW && row0 + cl < M) {
             float v = acc[0];
@@ -1136,7 +1167,7 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
                 if (cl == j) v = acc[j];
             out[row0 + cl] = v;
         }
-        if (ss_group && cl == POSTPRE_LANES - 1) out[M] = acc[RPW];
+        if (ss_group && cl == L - 1) out[M] = acc[RPW];
     }
 }
 
@@ -1172,22 +1203,10 @@ __global__ __launch_bounds__(64) void hc_finish_kernel(
         if constexpr (MODE == MODE_FUSED) lvs = load_vec<DT>(layer_out, t * d + c0);
     }
 
+    // the partials were written by other CUs: each batch is a trip past this
+    // XCD's L2
     float tot = 0.f;
-    if (lane <= M) {
-        const float *p = ws + t * (M + 1) + lane;
-        const size_t stride = (size_t)T * (M + 1);
-        // chunk order, PB loads in flight at a time (the partials were
-        // written by other CUs: each round is a trip past this XCD's L2)
-        int c = 0;
-        for (; c + PB <= P; c += PB) {
-            float v[PB];
-#pragma unroll
-            for (int k = 0; k < PB; ++k) v[k] = p[(size_t)(c + k) * stride];
-#pragma unroll
-            for (int k = 0; k < PB; ++k) tot += v[k];
-        }
-        for (; c < P; ++c) tot += p[(size_t)c * stride];
-    }
+    if (lane <= M) tot = sum_chunks<PB>(ws + t * (M + 1) + lane, (size_t)T * (M + 1), P);
     const float ssum = __shfl(tot, M, 64);
     const float r = sqrtf(ssum / (float)kfull + eps);  // kfull: all n*d columns, also when X is a share
     float z = 0.f;
@@ -1463,26 +1482,38 @@ hipError_t launch_hc(const FusedArgs &a, bool fused, int path, hipStream_t s) {
     }
 }
 
-template <int N, int DT>
-static hipError_t launch_post_pre_n(const FusedArgs &a, const float *coeffs_prev, hipStream_t s) {
+// The finish kernel sums the P2 chunk partials (PB = 64 in flight for the up
+// to 64 chunks of 16-lane chunking, 32 otherwise); the pre-mix reads X' back
+// from X_out, with no post update there, 64 * V columns per workgroup.
+template <int N, int DT, int L>
+static hipError_t launch_post_pre_nl(const FusedArgs &a, const float *coeffs_prev, hipStream_t s) {
     constexpr int V = StateVec<DT>::V;
-    const int P2 = post_pre_chunks(a.d, DT);
+    const int P2 = (a.d + L * V - 1) / (L * V);
     const dim3 g1((unsigned)((a.T + SPLITK_TOKENS - 1) / SPLITK_TOKENS), (unsigned)P2);
-    hipError_t e = launch_kernel(hc_postpre_partials_kernel<N, DT>, g1, dim3(64), s, a.d, (int)a.T,
+    hipError_t e = launch_kernel(hc_postpre_partials_kernel<N, DT, L>, g1, dim3(64), s, a.d, (int)a.T,
                                  a.X, coeffs_prev, a.layer_out, a.W, a.X_out, a.ws);
     if (e != hipSuccess) return e;
-    // the pre-mix reads X' back from X_out; no post update here. The finish
-    // kernel sums the P2 chunk partials; its pass 2 takes 64 * V columns per
-    // workgroup.
     const dim3 g2((unsigned)a.T, (unsigned)((a.d + 64 * V - 1) / (64 * V)));
-    return launch_kernel(hc_finish_kernel<N, DT, MODE_PRE, 32>, g2, dim3(64), s, a.d, N * a.d, (int)a.T, P2,
-                         a.eps, a.iters, (const void *)a.X_out, a.bias, (const float *)a.ws,
+    return launch_kernel(hc_finish_kernel<N, DT, MODE_PRE, L == 16 ? 64 : 32>, g2, dim3(64), s, a.d, N * a.d,
+                         (int)a.T, P2, a.eps, a.iters, (const void *)a.X_out, a.bias, (const float *)a.ws,
                          (const void *)nullptr, a.layer_in, a.coeffs, a.logits, (void *)nullptr);
+}
+
+template <int N, int DT>
+static hipError_t launch_post_pre_n(const FusedArgs &a, const float *coeffs_prev, hipStream_t s) {
+    return post_pre_lanes(a.d, DT) == 16 ? launch_post_pre_nl<N, DT, 16>(a, coeffs_prev, s)
+                                         : launch_post_pre_nl<N, DT, 32>(a, coeffs_prev, s);
+}
+
+int post_pre_lanes(int d, int dt) {
+    const int V = dt == DT_F32 ? 4 : 8;
+    return (d + 16 * V - 1) / (16 * V) <= 64 ? 16 : 32;
 }
 
 int post_pre_chunks(int d, int dt) {
     const int V = dt == DT_F32 ? 4 : 8;
-    return (d + POSTPRE_LANES * V - 1) / (POSTPRE_LANES * V);
+    const int L = post_pre_lanes(d, dt);
+    return (d + L * V - 1) / (L * V);
 }
 
 hipError_t launch_post_pre(const FusedArgs &a, const float *coeffs_prev, bool one_pass, int path,

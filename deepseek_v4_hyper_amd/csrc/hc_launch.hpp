@@ -48,6 +48,7 @@ hipError_t launch_partials(const FusedArgs &a, int path, hipStream_t s);
 // and pass 2 on the share a.X (width a.d) of a row n * d_total long.
 hipError_t launch_combine(const FusedArgs &a, int d_total, int G, const float *partials,
                           hipStream_t s);
+int post_pre_lanes(int d, int dt);   // lanes per column chunk of the one-pass step (16 or 32)
 int post_pre_chunks(int d, int dt);
 // Bytes of the device-resident scratch array behind ds4hc_post_pre_noalloc,
 // and its address on the current device (looked up once per device).

@@ -207,15 +207,20 @@ def post_pre(p, T=8, dt=B.DS4HC_F32, **over):
 
 def test_post_pre_workspace_bytes():
     p = B.make_params(4, 4096)
-    # one pass for T <= 160: column chunks of 32 lanes x V columns, (m + 1) floats per token
-    assert B.ds4hc_post_pre_workspace_bytes(p, 1, B.DS4HC_F32) == (4096 // 128) * 1 * 25 * 4
-    assert B.ds4hc_post_pre_workspace_bytes(p, 32, B.DS4HC_BF16) == (4096 // 256) * 32 * 25 * 4
-    assert B.ds4hc_post_pre_workspace_bytes(p, 160, B.DS4HC_F32) == 32 * 160 * 25 * 4
+    # one pass for T <= 160: column chunks of L lanes x V columns (L = 16 while that
+    # gives at most 64 chunks, else 32), (m + 1) floats per token
+    assert B.ds4hc_post_pre_workspace_bytes(p, 1, B.DS4HC_F32) == (4096 // 64) * 1 * 25 * 4
+    assert B.ds4hc_post_pre_workspace_bytes(p, 32, B.DS4HC_BF16) == (4096 // 128) * 32 * 25 * 4
+    assert B.ds4hc_post_pre_workspace_bytes(p, 160, B.DS4HC_F32) == 64 * 160 * 25 * 4
+    p7 = B.make_params(4, 7168)
+    assert B.ds4hc_post_pre_workspace_bytes(p7, 2, B.DS4HC_BF16) == (7168 // 128) * 2 * 25 * 4
+    assert B.ds4hc_post_pre_workspace_bytes(p7, 2, B.DS4HC_F32) == (7168 // 128) * 2 * 25 * 4  # 32 lanes
+    assert B.ds4hc_post_pre_workspace_bytes(B.make_params(4, 256), 1, B.DS4HC_F32) == 4 * 25 * 4
     # larger T: post, then the pre path (row-resident or tile: none)
     assert B.ds4hc_post_pre_workspace_bytes(p, 161, B.DS4HC_F32) == 0
     assert B.ds4hc_post_pre_workspace_bytes(p, 4096, B.DS4HC_F32) == 0
     pf = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_SPLITK)
-    assert B.ds4hc_post_pre_workspace_bytes(pf, 4096, B.DS4HC_F32) == 32 * 4096 * 25 * 4
+    assert B.ds4hc_post_pre_workspace_bytes(pf, 4096, B.DS4HC_F32) == 64 * 4096 * 25 * 4
     assert B.ds4hc_post_pre_workspace_bytes(B.make_params(3, 4096), 1, B.DS4HC_F32) == 0
 
 
