@@ -285,17 +285,21 @@ ds4hc_status ds4hc_post_pre_noalloc(const ds4hc_params *p, int64_t T, ds4hc_dtyp
 
 namespace {
 
-// Split-over-d partials: the tile kernel where it fits and T is large, else
-// split-K chunks of the share (workspace) summed into [T][m+1].
+// Split-over-d partials: for large T the streamed 16-token kernel, else split-K
+// chunks of the share (workspace) summed into [T][m+1]; FORCE_TILE takes the
+// tile kernel's partials mode.
 ds4hc_status make_partials_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *out) {
     const int n = p->n_hc, d = p->d, m = 2 * n + n * n;
     const uint32_t force = p->flags & FORCE_FLAGS;
     if (force == DS4HC_FLAG_FORCE_ROWRES) return DS4HC_ERR_UNSUPPORTED;
     const bool fits_tile = ds4hc::tile_steps(d, dt) <= ds4hc::tile_max_steps();
     Plan pl{ds4hc::PATH_SPLITK, 0, 0};
-    if (force == DS4HC_FLAG_FORCE_TILE || (force == 0 && T > SPLITK_MAX_T && fits_tile)) {
+    if (force == DS4HC_FLAG_FORCE_TILE) {
         if (!fits_tile) return DS4HC_ERR_UNSUPPORTED;
         pl.path = ds4hc::PATH_TILE;
+    } else if (force == 0 && T > SPLITK_MAX_T) {
+        if ((uint64_t)(T + 15) / 16 * 512u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
+        pl.path = ds4hc::PATH_STREAM;
     } else {
         pl.P = ds4hc::splitk_chunks(n, d, dt);
         const uint64_t tg = (uint64_t)(T + 3) / 4;

@@ -1018,6 +1018,166 @@ __global__ __launch_bounds__(64) void hc_partials_kernel(int d, int T, const voi
 }
 
 // ---------------------------------------------------------------------------
+// Split-over-d partials for large T, streamed: grid ceil(T / 16), 512 threads.
+// With no pass 2 the rows need not stay on chip, so a workgroup takes 16
+// tokens and streams their share rows, and the whole share weight, through
+// its CU once (the tile kernel's partials mode streams the weight once per 4
+// tokens). The flattened share row (K = n * d_s columns) is cut into k-steps
+// of 32 columns; wave w takes the w-th of eight contiguous runs of steps.
+// Lane l holds token l % 16 and columns 8 (l / 16) .. + 7 of a step: 32 bytes
+// of its token's row (16 for bfloat16) and 16 bytes of each of its W rows,
+// through buffer descriptors (rows past T or M and columns past K read zeros).
+// The fn dots are float32 MFMAs, v_mfma_f32_16x16x4_f32 with A = W (row
+// 16 b + l % 16 of block b, converted from f16 exactly) and B = x (token
+// l % 16), one instruction per column of the lane's eight: D[row][token]
+// gains the products of four columns, one per lane group. The sum of squares
+// is a per-lane VALU chain. A wave keeps one batch of SP_BATCH steps in flight
+// while it uses the other. Each wave's sums go to LDS and are added in wave
+// order (and lane-group order for the sum of squares), so the result does not
+// depend on timing.
+//
+// Measured on the prefill share (T = 4096, K = 4096, float32): the same loads
+// with the steps interleaved over the waves read the share at 4.2 TB/s against
+// 6.0 with contiguous runs (a token row is then read in 64-byte pieces
+// scattered over all the waves); 8-byte W loads per lane (16 columns per
+// step) left the load side alone at 22.7 us. The state loads keep the default
+// cache policy: the two 16-byte loads of a float32 lane each cover half of the
+// token's 128-byte line, and with the streaming (nt) policy the pass took 20.3
+// against 17.7 us. One step per batch: 17.0 us; two 17.7, four 23.
+// ---------------------------------------------------------------------------
+constexpr int SP_TOKENS = 16;
+constexpr int SP_WAVES = 8;
+constexpr int SP_BATCH = 1;  // k-steps of 32 columns per register batch (two batches)
+
+template <int N, int DT>
+__global__ __launch_bounds__(SP_WAVES * 64) void hc_stream_partials_kernel(int K, int T, const void *__restrict__ X,
+                                                                           const uint16_t *__restrict__ W,
+                                                                           float *__restrict__ out) {
+    constexpr int M = n_logits(N);
+    constexpr int RB = (M + 15) / 16;  // 16-row blocks of W
+    typedef float f4_t __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tok = lane & 15, grp = lane >> 4;
+    const int t0 = blockIdx.x * SP_TOKENS;
+    const int ntok = min(SP_TOKENS, T - t0);
+    constexpr int SB = DT == DT_F32 ? 4 : 2;
+    // Buffer loads: tokens past T (past this group's rows) and W rows past M
+    // lie past their descriptor's end, and columns past K take OOB_OFFSET, so
+    // all of them read zeros with no branch or select.
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc((const char *)X + (size_t)t0 * K * SB, (uint32_t)((size_t)ntok * K * SB));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)((size_t)M * K * 2));
+    const int nsteps = (K + 31) / 32;
+    const int per = (nsteps + SP_WAVES - 1) / SP_WAVES;
+    const int first = wave * per;
+    const int mine = max(0, min(per, nsteps - first));
+    __shared__ float red[SP_WAVES][M + 4][SP_TOKENS];
+
+    // Two batches of SP_BATCH steps in registers: while one is used, the
+    // other's loads are in flight. The batches swap roles every half of the
+    // loop, so the batch being used was always issued before the one in
+    // flight, on the way into the loop as on the way round it.
+    struct Batch {
+        StateVec<DT> x[SP_BATCH][8 / StateVec<DT>::V];
+        uint4 w[SP_BATCH][RB];
+    };
+    // steps i .. i + SP_BATCH - 1 of this wave (steps past its last read zeros)
+    auto fetch = [&](Batch &bt, int i) {
+#pragma unroll
+        for (int j = 0; j < SP_BATCH; ++j) {
+            const int k = (first + i + j) * 32 + 8 * grp;
+            const bool ok = i + j < mine && k < K;
+            // (offsets pinned in a register: given the constant OOB_OFFSET in
+            // one arm, the compiler otherwise branches between two loads)
+            int xo = ok ? (tok * K + k) * SB : OOB_OFFSET;
+            asm volatile("" : "+v"(xo));
+#pragma unroll
+            for (int h = 0; h < 8 / StateVec<DT>::V; ++h) {
+                const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 16 * h, 0));
+                if constexpr (DT == DT_F32)
+                    bt.x[j][h].raw = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                                 __uint_as_float(u.w));
+                else
+                    bt.x[j][h].raw = u;
+            }
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                int wo = ok ? ((16 * b + tok) * K + k) * 2 : OOB_OFFSET;
+                asm volatile("" : "+v"(wo));
+                bt.w[j][b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo, 0, 0));
+            }
+        }
+    };
+
+    f4_t acc[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) acc[b] = f4_t{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    auto use = [&](const Batch &bt) {
+#pragma unroll
+        for (int j = 0; j < SP_BATCH; ++j) {
+            float xf[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                constexpr int V = StateVec<DT>::V;
+                xf[e] = vec_get<DT>(bt.x[j][e / V], e % V);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(xf[e], xf[e], ss);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int b = 0; b < RB; ++b) {
+                    HalfVec<8> hv;
+                    hv.raw = bt.w[j][b];
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(half_get<8>(hv, e), xf[e], acc[b], 0, 0, 0);
+                }
+        }
+    };
+
+    // (scheduling barriers keep each batch's loads issued as a block, ahead
+    // of the use of the other batch)
+    Batch A, Bn;
+    fetch(A, 0);
+    for (int i0 = 0; i0 < mine; i0 += 2 * SP_BATCH) {
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(Bn, i0 + SP_BATCH);
+        __builtin_amdgcn_sched_barrier(0);
+        use(A);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(A, i0 + 2 * SP_BATCH);
+        __builtin_amdgcn_sched_barrier(0);
+        use(Bn);
+    }
+
+    // D layout: lane l holds rows 4 (l / 16) + r of its block, token l % 16
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * b + 4 * grp + r;
+            if (row < M) red[wave][row][tok] = acc[b][r];
+        }
+    red[wave][M + grp][tok] = ss;
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid < (M + 1) * SP_TOKENS) {
+        const int j = tid / SP_TOKENS, tk = tid % SP_TOKENS;
+        float v = 0.f;
+        if (j < M) {
+#pragma unroll
+            for (int w = 0; w < SP_WAVES; ++w) v += red[w][j][tk];
+        } else {
+#pragma unroll
+            for (int w = 0; w < SP_WAVES; ++w)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) v += red[w][M + g][tk];
+        }
+        if (t0 + tk < T) out[(size_t)(t0 + tk) * (M + 1) + j] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Split-over-d partials for small T: the split-K chunk partials of one column
 // share summed in chunk order into out[t][0..M] (dots, then sum of squares).
 // Grid (T), one wavefront.
@@ -1542,6 +1702,10 @@ hipError_t launch_post_pre(const FusedArgs &a, const float *coeffs_prev, bool on
 template <int N, int DT>
 static hipError_t launch_partials_n(const FusedArgs &a, int path, hipStream_t s) {
     if (path == PATH_TILE) return launch_tile_n<N, DT, MODE_PARTIALS>(tile_steps(a.d, DT), a, s);
+    if (path == PATH_STREAM)
+        return launch_kernel(hc_stream_partials_kernel<N, DT>,
+                             dim3((unsigned)((a.T + SP_TOKENS - 1) / SP_TOKENS)), dim3(SP_WAVES * 64), s,
+                             N * a.d, (int)a.T, a.X, a.W, a.logits);
     const int P = splitk_chunks(N, a.d, DT);
     const dim3 g1((unsigned)((a.T + SPLITK_TOKENS - 1) / SPLITK_TOKENS), (unsigned)P);
     hipError_t e = launch_kernel(hc_partials_kernel<N, DT>, g1, dim3(64), s, a.d, (int)a.T, a.X,

@@ -27,7 +27,7 @@ struct FusedArgs {
 };
 
 // Kernel paths for HC-pre / fused.
-enum : int { PATH_ROWRES = 0, PATH_TILE = 1, PATH_SPLITK = 2 };
+enum : int { PATH_ROWRES = 0, PATH_TILE = 1, PATH_SPLITK = 2, PATH_STREAM = 3 };  // STREAM: partials only
 
 int rowres_chunks(int d, int dt);
 int rowres_max_chunks(int n, int dt);

@@ -48,7 +48,8 @@ def _load():
         lib.ds4hc_oracle_sinkhorn.argtypes = [i64, ci, ci, _D, _D]
         lib.ds4hc_oracle_post.argtypes = [i64, ci, ci, _D, _D, _D, _D]
         lib.ds4hc_oracle_fused.argtypes = [i64, ci, ci, _D, _D, _D, _D, cd, ci, _D, _D, _D]
-        for f in ("pre", "sinkhorn", "post", "fused"):
+        lib.ds4hc_oracle_partials.argtypes = [i64, ci, ci, _D, _D, _D]
+        for f in ("pre", "sinkhorn", "post", "fused", "partials"):
             getattr(lib, "ds4hc_oracle_" + f).restype = ci
         lib.ds4hc_oracle_num_threads.restype = ci
         lib.ds4hc_oracle_set_threads.argtypes = [ci]
@@ -131,6 +132,19 @@ def fused(X, W, b, layer_out, eps=1e-6, iters=20):
     if rc:
         raise ValueError("ds4hc_oracle_fused rejected its arguments")
     return layer_in, coeffs, out
+
+
+def partials(X_share, W_share):
+    """Split-over-d partial sums of one column share: X_share [T, n, ds],
+    W_share [m, n*ds]. Returns [T, m+1]: the unnormalised fn dots, then the sum of squares."""
+    X, W = _f64(X_share), _f64(W_share)
+    T, n, ds = X.shape
+    m = n_logits(n)
+    assert W.shape == (m, n * ds)
+    out = np.empty((T, m + 1))
+    if _load().ds4hc_oracle_partials(T, n, ds, _p(X), _p(W), _p(out)):
+        raise ValueError("ds4hc_oracle_partials rejected its arguments")
+    return out
 
 
 def chain(X0, Ws, b, noise, eps=1e-6, iters=20, layer_scale=0.5):

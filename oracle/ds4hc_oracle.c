@@ -34,6 +34,13 @@
  *   6. layer_in[c] = sum_i pre_i * X[i][c]              (pre-mix)
  *   7. X'[i][c] = sum_j H[i][j] * X[j][c] + post_i * layer_out[c]  (hc_post)
  *
+ * Split over d (lucebox PR #507, Implementation: the HC state crosses the
+ * device boundary whole): r is one number per token, so
+ * z_j = (sum_k W[j][k] x_k) / r + b_j, and steps 1 and 3 need only the
+ * per-token sums S_j = sum_k W[j][k] x_k and Q = sum_k x_k^2, which add
+ * over any partition of the columns. ds4hc_oracle_partials computes them
+ * for one share of the columns.
+ *
  * Readings where the pages are silent (stated constants of the library):
  * eps inside the square root and added to the mean over all K elements;
  * no learned gain; logits ordered pre | post | residual (row-major,
@@ -235,6 +242,36 @@ int ds4hc_oracle_post(int64_t T, int n, int d, const double *X, const double *co
 }
 
 /* Whole op (steps 1-7) for a layer_out that does not depend on layer_in. */
+/* Split-over-d partial sums of one column share: X_share [T][n][ds],
+ * W_share [m][n*ds] (W's columns of the share, per stream), out [T][m+1]:
+ * out[t][j] = sum_k W_share[j][k] x_k (j < m), out[t][m] = sum_k x_k^2. */
+int ds4hc_oracle_partials(int64_t T, int n, int ds, const double *X_share,
+                          const double *W_share, double *out)
+{
+    if (bad_shape(T, n, ds) || !X_share || !W_share || !out)
+        return ORACLE_BAD_ARG;
+    const int m = n_logits(n);
+    const int64_t K = (int64_t)n * ds;
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        const double *x = X_share + (size_t)t * (size_t)K;
+        double *o = out + (size_t)t * (size_t)(m + 1);
+        for (int j = 0; j < m; ++j) {
+            const double *wj = W_share + (size_t)j * (size_t)K;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += wj[k] * x[k];
+            o[j] = acc;
+        }
+        double q = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            q += x[k] * x[k];
+        o[m] = q;
+    }
+    return ORACLE_OK;
+}
+
 int ds4hc_oracle_fused(int64_t T, int n, int d, const double *X, const double *W,
                        const double *b, const double *layer_out, double eps, int iters,
                        double *layer_in, double *coeffs, double *X_out)

@@ -509,6 +509,46 @@ def test_split_over_d(dtype, G, n, d, T):
     check_full(case, got, f"split d G={G} T={T}")
 
 
+def _check_partials(got, ref, Xs, Ws, what):
+    """Dots within 2e-6 of sum_k |W_jk x_k| (float32 accumulation over K terms),
+    the sum of squares within 2e-6 relative."""
+    m = Ws.shape[0]
+    T = Xs.shape[0]
+    x = Xs.reshape(T, -1)
+    scale = np.abs(x) @ np.abs(Ws).T
+    err = np.abs(got[:, :m] - ref[:, :m])
+    assert np.all(err <= 2e-6 * scale + 1e-30), f"{what}: dots max err/scale {np.max(err / (scale + 1e-300)):.3g}"
+    rel = np.abs(got[:, m] - ref[:, m]) / np.maximum(ref[:, m], 1e-300)
+    assert np.all((rel <= 2e-6) | (ref[:, m] == 0)), f"{what}: sum of squares max rel {np.max(rel):.3g}"
+    say(f"    {what}: dots max err/scale {np.max(err / (scale + 1e-300)):.2e}, sum of squares max rel {np.max(rel):.2e}")
+
+
+@pytest.mark.parametrize("path,dtype,n,ds,T", [
+    ("default", wl.F32, 4, 1024, 4096),    # the prefill share the benchmark times (streamed kernel)
+    ("default", wl.BF16, 4, 1792, 4096),   # a quarter of the stress width
+    ("default", wl.F32, 2, 264, 700),      # K = 528: a partial last k-step, a partial token group
+    ("default", wl.BF16, 1, 520, 161),     # n = 1 (one 16-row block), K = 520
+    ("default", wl.F32, 4, 1024, 37),      # split-K chunks at small T
+    ("tile", wl.F32, 4, 1024, 700),
+    ("tile", wl.BF16, 2, 264, 161),
+    ("splitk", wl.BF16, 4, 1024, 700),
+])
+def test_partials_against_oracle(path, dtype, n, ds, T):
+    """ds4hc_partials of one column share against the oracle's partial sums, on
+    every path that can produce them."""
+    torch = torch_mod()
+    case = wl.make_random(60 + T + n, T, n, ds, dtype)
+    X, W, _, _ = case_to_device(case)
+    flags = {"default": 0, "tile": B.DS4HC_FLAG_FORCE_TILE, "splitk": B.DS4HC_FLAG_FORCE_SPLITK}[path]
+    say(f"[gpu] ds4hc_partials path={path} T={T} n={n} d_s={ds} {dtype}")
+    got = B.ds4hc_partials(X, W, flags=flags)
+    torch.cuda.synchronize()
+    Xs = wl.state_to_f64(case.X, dtype)
+    Ws = np.asarray(case.W, dtype=np.float64)
+    ref = oracle.partials(Xs, Ws)
+    _check_partials(got.cpu().numpy().astype(np.float64), ref, Xs, Ws, f"partials {path}")
+
+
 # ------------------------------------------------------------------ 86-site decode chain, eager and graph
 
 def _chain_86(torch, case, b, Ws, noise, states, ins, coeffs, ws, wsb):

@@ -290,6 +290,53 @@ def test_nan_stays_in_its_token():
         np.testing.assert_array_equal(out[t], out2[t])
 
 
+# ---------------------------------------------------------------- split-over-d partial sums
+
+def _share(X, W, g, G):
+    T, n, d = X.shape
+    ds = d // G
+    Xs = X[:, :, g * ds:(g + 1) * ds]
+    Ws = W.reshape(W.shape[0], n, d)[:, :, g * ds:(g + 1) * ds].reshape(W.shape[0], n * ds)
+    return np.ascontiguousarray(Xs), np.ascontiguousarray(Ws)
+
+
+def test_partials_give_the_pre_logits():
+    """The unnormalised dots over 1/r plus the bias are HC-pre's logits, with r
+    from the sum of squares (r is one number per token)."""
+    X, W, b, _ = rand_case(31, 9, 4, 24)
+    m, K, eps = wl.n_logits(4), 4 * 24, 1e-6
+    P = oracle.partials(X, W)
+    r = np.sqrt(P[:, m] / K + eps)
+    z = P[:, :m] / r[:, None] + b
+    _, _, logits = oracle.pre(X, W, b, eps=eps)
+    np.testing.assert_allclose(z, logits, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(P[:, m], (X.reshape(9, K) ** 2).sum(axis=1), rtol=1e-13)
+
+
+@pytest.mark.parametrize("n,d,i0,c0", [(4, 8, 2, 5), (2, 12, 1, 3)])
+def test_partials_of_one_hot_state(n, d, i0, c0):
+    """x = c at stream i0, column c0: the dots are c times W's column i0*d + c0
+    and the sum of squares is c^2, exactly (pins W's orientation and the
+    flattening k = i*d + c)."""
+    m = wl.n_logits(n)
+    W = rng(5).standard_normal((m, n * d))
+    X = np.zeros((1, n, d))
+    X[0, i0, c0] = 2.5
+    P = oracle.partials(X, W)
+    np.testing.assert_array_equal(P[0, :m], 2.5 * W[:, i0 * d + c0])
+    assert P[0, m] == 6.25
+
+
+@pytest.mark.parametrize("G", [2, 3])
+def test_partials_add_over_column_shares(G):
+    """Each stream's columns split into G shares: the shares' partial sums add up
+    to the whole row's."""
+    X, W, b, _ = rand_case(32, 7, 4, 24)
+    whole = oracle.partials(X, W)
+    parts = sum(oracle.partials(*_share(X, W, g, G)) for g in range(G))
+    np.testing.assert_allclose(parts, whole, rtol=1e-12, atol=1e-12)
+
+
 def test_thread_count_does_not_change_bits():
     X, W, b, lo = rand_case(19, 37, 4, 16)
     nt = oracle.num_threads()
