@@ -212,7 +212,8 @@ size_t ds4hc_post_pre_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dt
  * address (hipGetSymbolAddress) and keeps it.
  * Limit: a call whose ds4hc_post_pre_workspace_bytes(p, T, dtype) exceeds
  * DS4HC_NOALLOC_SCRATCH_BYTES returns DS4HC_ERR_UNSUPPORTED and enqueues
- * nothing (n = 4: T * ceil(d / (32 * V)) * 100 bytes, V = 4 for float32 and 8
+ * nothing (n = 4: T * P * 100 bytes with P = ceil(d / (16 * V)) column chunks
+ * where that is at most 64, else ceil(d / (32 * V)); V = 4 for float32 and 8
  * for bfloat16 state; d = 4096 float32 fits every T of the one-pass path).
  * All calls on one device share that device's array, and the kernels
  * overwrite every byte they read before reading it (nothing must start at
@@ -240,7 +241,9 @@ ds4hc_status ds4hc_post_pre_noalloc(const ds4hc_params *p, int64_t T, ds4hc_dtyp
  *   X_share   [T, n, d_s]    state dtype   (read)
  *   W_share   [m, n * d_s]   float16 bits  (read) W's columns i*d + share, per stream i
  *   partials  [T, m + 1]     float32       (written)
- *   workspace >= ds4hc_partials_workspace_bytes(p, T, dtype) bytes
+ *   workspace >= ds4hc_partials_workspace_bytes(p, T, dtype) bytes (0 for
+ *               T > 160: a streamed kernel, 16 tokens per workgroup, writes the
+ *               partials directly; split-K chunks below, or when forced)
  */
 ds4hc_status ds4hc_partials(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, const void *X_share,
                             const uint16_t *W_share, float *partials, void *workspace,

@@ -261,7 +261,9 @@ def test_partials_workspace_bytes():
     p = B.make_params(4, 1024)   # a quarter share of d = 4096
     P = (4 * 1024) // 256
     assert B.ds4hc_partials_workspace_bytes(p, 1, B.DS4HC_F32) == P * 1 * 25 * 4
-    assert B.ds4hc_partials_workspace_bytes(p, 4096, B.DS4HC_F32) == 0   # tile kernel, partials mode
+    assert B.ds4hc_partials_workspace_bytes(p, 4096, B.DS4HC_F32) == 0   # streamed 16-token kernel
+    pt = B.make_params(4, 1024, flags=B.DS4HC_FLAG_FORCE_TILE)
+    assert B.ds4hc_partials_workspace_bytes(pt, 4096, B.DS4HC_F32) == 0  # tile kernel, partials mode
     pr = B.make_params(4, 1024, flags=B.DS4HC_FLAG_FORCE_ROWRES)
     assert B.ds4hc_partials_workspace_bytes(pr, 8, B.DS4HC_F32) == 0      # unsupported -> 0
 
