@@ -11,9 +11,11 @@ Prints one JSON line. Three input sets are rotated so no step starts with its
 inputs warm in the 256 MiB last-level cache. Before the warm-up steps the op
 runs for ~100 ms of wall time, so the timed steps see steady clocks however
 few warm-up steps are asked for. Besides the headline figures the line holds:
-the bandwidth of a plain 1 GiB device copy (libds4hc_bw.so) measured in the
-same process, and the op's fraction of it, the per-call latency of the decode-sized workloads
-(T=1, d=256 and T=4, d=4096) warm and with the caches flushed, and the CPU
+the GPU's shader and memory clocks and package power cap as rocm-smi reports
+them while the op runs (after the timed steps), the bandwidth of a plain
+1 GiB device copy (libds4hc_bw.so) measured in the same process, and the op's
+fraction of it, the per-call latency of the decode-sized workloads (T=1,
+d=256 and T=4, d=4096) warm and with the caches flushed, and the CPU
 baseline: the fp64 oracle on the same workload with all host cores, and with
 one thread on a sample of it.
 """
@@ -102,6 +104,49 @@ def cpu_info():
     except AttributeError:
         usable = os.cpu_count()
     return model, os.cpu_count(), usable
+
+
+def gpu_clocks(step, seconds_max=8.0):
+    """GPU clocks and package power cap as rocm-smi reports them while the op runs
+    back to back (outside the timed region): {"sclk_mhz", "mclk_mhz", "power_cap_w"},
+    or None where rocm-smi is missing or says nothing. rocm-smi runs as a child
+    process; the op keeps the GPU busy until it has answered."""
+    import shutil
+    import subprocess
+    import torch
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    if not os.path.exists(exe):
+        return None
+    try:
+        p = subprocess.Popen([exe, "--showclocks", "--showmaxpower", "--json"], stdout=subprocess.PIPE,
+                             stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0, i = time.time(), 0
+    while p.poll() is None and time.time() - t0 < seconds_max:
+        for _ in range(50):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    try:
+        out, _ = p.communicate(timeout=10)
+    except subprocess.TimeoutExpired:
+        p.kill()
+        p.communicate()
+        return None
+    try:
+        card = next(iter(json.loads(out).values()))
+    except (ValueError, StopIteration, AttributeError):
+        return None
+
+    def num(key):
+        v = card.get(key)
+        if v is None:
+            return None
+        digits = "".join(ch for ch in str(v) if ch.isdigit() or ch == ".")
+        return float(digits) if digits else None
+    return {"sclk_mhz": num("sclk clock speed:"), "mclk_mhz": num("mclk clock speed:"),
+            "power_cap_w": num("Max Graphics Package Power (W)"), "sampled": "rocm-smi during back-to-back steps"}
 
 
 def _time_oracle(fn, min_runs, min_seconds, max_runs):
@@ -566,6 +611,7 @@ def main():
 
     extras = {}
     if not args.no_extras:
+        extras["clocks"] = gpu_clocks(step)
         extras["copy_gbps"] = copy_bandwidth()
         extras["latency"] = latency_records()
     if args.copy_calibration:
@@ -604,6 +650,7 @@ def main():
         rec["roofline"]["copy_gbps"] = extras["copy_gbps"]
         rec["roofline"]["frac_of_copy"] = achieved / extras["copy_gbps"]
         rec["latency_us"] = extras["latency"]
+        rec["gpu_clocks"] = extras["clocks"]
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(c0)
     print(json.dumps(rec), flush=True)
