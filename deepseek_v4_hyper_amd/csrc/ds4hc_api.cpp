@@ -28,6 +28,9 @@ constexpr int64_t ROWRES_MAX_T = 384;      // then the row-resident kernel up to
 constexpr int64_t MAX_T = int64_t(1) << 24;
 constexpr int MAX_ITERS = 1000;
 constexpr uint64_t MAX_WORK_ITEMS = 0xFFFFFFFFull;  // HSA dispatch grid size is 32-bit
+// The streamed partials kernel forms 32-bit byte offsets up to 64 * n * d_s;
+// longer share rows take split-K.
+constexpr uint64_t STREAM_MAX_K = uint64_t(1) << 24;
 constexpr uint32_t FORCE_FLAGS =
     DS4HC_FLAG_FORCE_ROWRES | DS4HC_FLAG_FORCE_TILE | DS4HC_FLAG_FORCE_SPLITK;
 constexpr uint32_t KNOWN_FLAGS = DS4HC_FLAG_DETERMINISTIC | FORCE_FLAGS;
@@ -297,7 +300,7 @@ ds4hc_status make_partials_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt
     if (force == DS4HC_FLAG_FORCE_TILE) {
         if (!fits_tile) return DS4HC_ERR_UNSUPPORTED;
         pl.path = ds4hc::PATH_TILE;
-    } else if (force == 0 && T > SPLITK_MAX_T) {
+    } else if (force == 0 && T > SPLITK_MAX_T && (uint64_t)n * d <= STREAM_MAX_K) {
         if ((uint64_t)(T + 15) / 16 * 512u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
         pl.path = ds4hc::PATH_STREAM;
     } else {

@@ -266,6 +266,10 @@ def test_partials_workspace_bytes():
     assert B.ds4hc_partials_workspace_bytes(pt, 4096, B.DS4HC_F32) == 0  # tile kernel, partials mode
     pr = B.make_params(4, 1024, flags=B.DS4HC_FLAG_FORCE_ROWRES)
     assert B.ds4hc_partials_workspace_bytes(pr, 8, B.DS4HC_F32) == 0      # unsupported -> 0
+    # share rows past 2^24 columns (n * d_s) leave the streamed kernel (32-bit offsets) for split-K
+    assert B.ds4hc_partials_workspace_bytes(B.make_params(4, 1 << 22), 200, B.DS4HC_F32) == 0
+    big = B.make_params(4, (1 << 22) + 8)   # bfloat16: split-K takes up to 65535 chunks of 512 columns
+    assert B.ds4hc_partials_workspace_bytes(big, 200, B.DS4HC_BF16) == (4 * ((1 << 22) + 8) + 511) // 512 * 200 * 25 * 4
 
 
 @no_gpu_only
