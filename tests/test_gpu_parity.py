@@ -699,6 +699,40 @@ def test_deterministic_20_repeats(workload):
     say(f"    sha256 {h0[:16]}... stable over 20 runs")
 
 
+@pytest.mark.parametrize("T", [4096, 37])
+def test_deterministic_20_repeats_split_over_d(T):
+    """The split over d is bit-stable run to run: 20 runs of ds4hc_partials on one
+    1024-column share of the prefill state (T = 4096: the streamed kernel; T = 37:
+    split-K), each after a call on other inputs, and the combine of the four shares'
+    partials, all bitwise identical."""
+    torch = torch_mod()
+    case = wl.make_prefill(5, T=T)
+    X, W, b, lo, sh = _shares(case, 4)
+    noise = wl.make_random(98, 53, case.n, 1024, case.dtype)
+    Xn, Wn, _, _ = case_to_device(noise)
+    say(f"[gpu] 20 repeats of ds4hc_partials + ds4hc_combine, prefill share T={T}")
+    fl = B.DS4HC_FLAG_DETERMINISTIC
+
+    def run():
+        P = torch.stack([B.ds4hc_partials(xs, ws, flags=fl) for xs, ws, _ in sh])
+        out = B.ds4hc_combine(P, b, sh[0][0], sh[0][2], case.d)
+        return (P,) + tuple(out)
+
+    first = run()
+    torch.cuda.synchronize()
+    h0 = _sha(first)
+    for r in range(1, 20):
+        B.ds4hc_partials(Xn, Wn, flags=fl)
+        outs = run()
+        torch.cuda.synchronize()
+        for a, e in zip(outs, first):
+            assert torch.equal(_bits(a), _bits(e)), f"repeat {r} differs"
+        if r == 19:
+            assert _sha(outs) == h0
+        del outs
+    say(f"    sha256 {h0[:16]}... stable over 20 runs")
+
+
 def test_deterministic_20_repeats_chain():
     """The 43-layer decode chain (ds4hc_pre, then one ds4hc_post_pre per layer
     boundary, then ds4hc_post), 20 runs: every layer's layer_in and coefficients
