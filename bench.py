@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "HC-op tokens/s and achieved HBM GB/s (% of peak) at T=4096, d=4096, n_hc=4"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_NAME = {"default": "hc_tile_kernel", "tile": "hc_tile_kernel", "rowres": "hc_rowres_kernel",
-               "splitk": "hc_partials_kernel+hc_finish_kernel"}
+               "splitk": "hc_colchunk_partials_kernel+hc_finish_kernel"}
 COUNTERS_FILE = {"prefill": "profiles/hc_tile_prefill_T4096_counters.json",
                  "stress": "profiles/hc_tile_stress_T16384_counters.json"}
 

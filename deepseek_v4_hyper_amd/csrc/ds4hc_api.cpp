@@ -115,7 +115,7 @@ ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *o
     } else if (path == ds4hc::PATH_TILE) {
         // persistent grid: at most one workgroup per CU, whatever T is
     } else {
-        pl.P = ds4hc::splitk_chunks(n, d, dt);
+        pl.P = ds4hc::colchunk_chunks(d, dt);
         const uint64_t tg = (uint64_t)(T + 3) / 4;
         const uint64_t cb = (uint64_t)(d + 64 * vec_elems(dt) - 1) / (64 * vec_elems(dt));
         // partials grid (token groups, P), finish grid (T, column blocks)
@@ -188,7 +188,7 @@ ds4hc_status make_post_pre_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt
     pp.one_pass = force == DS4HC_FLAG_FORCE_SPLITK || (force == 0 && T <= SPLITK_MAX_T);
     if (pp.one_pass) {
         const int m = 2 * p->n_hc + p->n_hc * p->n_hc;
-        const uint64_t P2 = (uint64_t)ds4hc::post_pre_chunks(p->d, dt);
+        const uint64_t P2 = (uint64_t)ds4hc::colchunk_chunks(p->d, dt);
         const uint64_t tg = (uint64_t)(T + 3) / 4;
         if (tg * 64u > MAX_WORK_ITEMS || P2 > 0xFFFFu || (uint64_t)T * 64u > MAX_WORK_ITEMS)
             return DS4HC_ERR_UNSUPPORTED;
@@ -304,7 +304,7 @@ ds4hc_status make_partials_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt
         if ((uint64_t)(T + 15) / 16 * 512u > MAX_WORK_ITEMS) return DS4HC_ERR_UNSUPPORTED;
         pl.path = ds4hc::PATH_STREAM;
     } else {
-        pl.P = ds4hc::splitk_chunks(n, d, dt);
+        pl.P = ds4hc::colchunk_chunks(d, dt);
         const uint64_t tg = (uint64_t)(T + 3) / 4;
         if (tg * 64u > MAX_WORK_ITEMS || pl.P > 0xFFFF || (uint64_t)T * 64u > MAX_WORK_ITEMS)
             return DS4HC_ERR_UNSUPPORTED;

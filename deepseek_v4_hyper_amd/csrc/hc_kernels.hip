@@ -964,60 +964,6 @@ __device__ __forceinline__ float sum_chunks(const float *__restrict__ p, size_t 
 }
 
 // ---------------------------------------------------------------------------
-// Split-K partials: grid (ceil(T / SPLITK_TOKENS), P chunks), one wavefront.
-// Chunk p covers flattened columns [p*64*V, (p+1)*64*V) of K; lane l owns V
-// consecutive columns. Writes ws[p][t][0..M) = partial dots, ws[p][t][M] =
-// partial sum of squares.
-// ---------------------------------------------------------------------------
-template <int N, int DT>
-__global__ __launch_bounds__(64) void hc_partials_kernel(int d, int T, const void *__restrict__ X,
-                                                         const uint16_t *__restrict__ W,
-                                                         float *__restrict__ ws) {
-    constexpr int V = StateVec<DT>::V;
-    constexpr int M = n_logits(N);
-    const int lane = threadIdx.x;
-    const size_t K = (size_t)N * d;
-    const size_t k0 = ((size_t)blockIdx.y * 64 + lane) * V;
-    const bool ok = k0 < K;
-    const int tbase = blockIdx.x * SPLITK_TOKENS;
-
-    HalfVec<V> w[M];
-#pragma unroll
-    for (int j = 0; j < M; ++j) {
-        if (ok)
-            w[j] = load_half_vec<V>(W + (size_t)j * K + k0);
-        else
-            w[j].raw = {};
-    }
-
-#pragma unroll
-    for (int tt = 0; tt < SPLITK_TOKENS; ++tt) {
-        const int t = tbase + tt;
-        if (t >= T) break;  // uniform across the wavefront
-        const StateVec<DT> xv = ok ? load_vec<DT>(X, (size_t)t * K + k0) : zero_vec<DT>();
-        float acc[M + 1];
-#pragma unroll
-        for (int j = 0; j <= M; ++j) acc[j] = 0.f;
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-            const float x = vec_get<DT>(xv, e);
-            acc[M] = fmaf(x, x, acc[M]);
-#pragma unroll
-            for (int j = 0; j < M; ++j) acc[j] = fmaf(half_get<V>(w[j], e), x, acc[j]);
-        }
-#pragma unroll
-        for (int j = 0; j <= M; ++j) acc[j] = wave_sum(acc[j]);
-        if (lane <= M) {
-            float v = acc[0];
-#pragma unroll
-            for (int j = 1; j <= M; ++j)
-                if (lane == j) v = acc[j];
-            ws[((size_t)blockIdx.y * T + t) * (M + 1) + lane] = v;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Split-over-d partials for large T, streamed: grid ceil(T / 16), 512 threads.
 // With no pass 2 the rows need not stay on chip, so a workgroup takes 16
 // tokens and streams their share rows, and the whole share weight, through
@@ -1193,23 +1139,31 @@ __global__ __launch_bounds__(64) void hc_chunk_sum_kernel(int T, int P, const fl
 }
 
 // ---------------------------------------------------------------------------
-// One-pass chain step, split-K part: grid (ceil(T / SPLITK_TOKENS), P2), one
+// Split-K partials over column chunks: grid (ceil(T / SPLITK_TOKENS), P), one
 // wavefront. With L lanes per column chunk (16 or 32), chunk p covers columns
 // [p*L*V, (p+1)*L*V) of every stream: lane l = L g + c holds the V columns
-// p*L*V + c*V .. of all n streams, so it can apply the previous site's post
-// update X' = H.X + post (x) layer_out itself (same operation order as
-// hc_post_kernel, so X' is bitwise what ds4hc_post writes); the 64 / L lane
-// groups g hold the same columns and split the M fn rows of the next site
-// (rows g*RPW ..), and group 0 stores X'. Writes the partial dots of the next
-// site's fn projection and the partial sum of squares of X' (as rounded to the
-// state type) to ws[p][t][0..M].
+// p*L*V + c*V .. of all n streams, and the 64 / L lane groups g hold the same
+// columns and split the M fn rows (rows g*RPW ..), so each lane sums only its
+// group's rows over 16 or 32 lanes. Writes the partial dots and the partial
+// sum of squares to ws[p][t][0..M]; the finish kernel (or the chunk sum of the
+// split over d) adds them in chunk order.
 //
-// At decode sizes the step is latency-bound: narrower chunks spread W over
+// POST = false: the partials of X itself (split-K HC-pre, and the split over
+// d at small T). POST = true: the one-pass chain step; a lane first applies
+// the previous site's post update X' = H.X + post (x) layer_out to its columns
+// (same operation order as hc_post_kernel, so X' is bitwise what ds4hc_post
+// writes), group 0 stores X', and the partials are those of X' as stored
+// (rounded to the state type).
+//
+// At decode sizes the pass is latency-bound: narrower chunks spread W over
 // more CUs and give each lane fewer loads, but add partials for the finish
-// kernel to combine. post_pre_lanes() takes 16 lanes while that gives at most
+// kernel to combine. colchunk_lanes() takes 16 lanes while that gives at most
 // 64 chunks, else 32. Graph-replayed ds4hc_post_pre at T = 1, 16 against 32
 // lanes: d = 4096 fp32 6.2 / 6.7 us, d = 7168 bf16 8.0 / 8.3 us, d = 7168 fp32
-// (112 chunks at 16 lanes) 8.0 / 7.7 us.
+// (112 chunks at 16 lanes) 8.0 / 7.7 us. For HC-pre this layout replaced
+// chunks of 64 lanes over the flattened row, each lane summing all M + 1
+// values over the whole wave per token: ds4hc_fused at T = 4, d = 4096 fp32
+// 11.4 -> 7.7 us, at T = 1 7.4 -> 6.1 us.
 // ---------------------------------------------------------------------------
 
 // Sum over the L lanes of a column chunk (every lane gets the total): within
@@ -1229,8 +1183,8 @@ __device__ __forceinline__ float chunk_sum(float v) {
     return v;
 }
 
-template <int N, int DT, int L>
-__global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
+template <int N, int DT, int L, bool POST>
+__global__ __launch_bounds__(64) void hc_colchunk_partials_kernel(
     int d, int T, const void *__restrict__ X, const float *__restrict__ coeffs_prev,
     const void *__restrict__ layer_out, const uint16_t *__restrict__ W, void *X_out,
     float *__restrict__ ws) {
@@ -1248,10 +1202,10 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
     const int cs = ok ? c0 : 0;                // in-bounds column for every lane
     const int tbase = blockIdx.x * SPLITK_TOKENS;
 
-    // The next site's weights for this lane's rows and columns, loaded once for
-    // all tokens of the group and first of all: they do not depend on the post
-    // update, so their round trip overlaps that of the state and the previous
-    // coefficients instead of following it (T = 1, d = 4096: the kernel's
+    // The (next site's) weights for this lane's rows and columns, loaded once
+    // for all tokens of the group and first of all: they do not depend on the
+    // post update, so their round trip overlaps that of the state and the
+    // previous coefficients instead of following it (T = 1, d = 4096: the
     // weight loads used to be issued only after the post update, itself after
     // four dependent loads of the coefficients). Rows past M (last group when 4
     // does not divide M) read row M - 1 and are never stored; lanes past d read
@@ -1270,21 +1224,31 @@ __global__ __launch_bounds__(64) void hc_postpre_partials_kernel(
     for (int tt = 0; tt < SPLITK_TOKENS; ++tt) {
         const int t = tbase + tt;
         if (t >= T) break;  // uniform across the wavefront
-        // the previous site's coefficients, the state and layer_out: all loads
-        // issued together, before the first store
+        // (the previous site's coefficients,) the state (and layer_out): all
+        // loads issued together, before the first store
         float cp[M];
+        StateVec<DT> lv;
+        if constexpr (POST) {
 #pragma unroll
-        for (int j = 0; j < M; ++j) cp[j] = coeffs_prev[(size_t)t * M + j];
+            for (int j = 0; j < M; ++j) cp[j] = coeffs_prev[(size_t)t * M + j];
+        }
         StateVec<DT> xin[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) xin[i] = load_vec<DT>(X, (size_t)t * K + (size_t)i * d + cs);
-        const StateVec<DT> lv = load_vec<DT>(layer_out, (size_t)t * d + cs);
+        if constexpr (POST) lv = load_vec<DT>(layer_out, (size_t)t * d + cs);
         float x[N][V];
         float acc[RPW + 1];
 #pragma unroll
         for (int j = 0; j <= RPW; ++j) acc[j] = 0.f;
+        if constexpr (!POST) {
+            // lanes past d contribute zeros
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int e = 0; e < V; ++e) x[i][e] = ok ? vec_get<DT>(xin[i], e) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < N && POST; ++i) {
             float o[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) {
@@ -1579,18 +1543,33 @@ static hipError_t launch_tile_n(int cs, const FusedArgs &a, hipStream_t s) {
 #undef DS4HC_TILE_CASE
 }
 
-template <int N, int DT, int MODE>
-static hipError_t launch_splitk_n(const FusedArgs &a, hipStream_t s) {
-    constexpr int V = StateVec<DT>::V;
-    const int P = splitk_chunks(N, a.d, DT);
+// Column-chunk partials of X (POST = false) into the workspace: P chunks of L lanes.
+template <int N, int DT, int L>
+static hipError_t launch_colchunk_pre(const FusedArgs &a, int P, hipStream_t s) {
     const dim3 g1((unsigned)((a.T + SPLITK_TOKENS - 1) / SPLITK_TOKENS), (unsigned)P);
-    hipError_t e = launch_kernel(hc_partials_kernel<N, DT>, g1, dim3(64), s, a.d, (int)a.T, a.X,
-                                 a.W, a.ws);
+    return launch_kernel(hc_colchunk_partials_kernel<N, DT, L, false>, g1, dim3(64), s, a.d, (int)a.T, a.X,
+                         (const float *)nullptr, (const void *)nullptr, a.W, (void *)nullptr, a.ws);
+}
+
+// Split-K HC-pre / fused: the column-chunk partials, then the finish kernel,
+// which sums the P partials (PB = 64 in flight for the up to 64 chunks of
+// 16-lane chunking, 32 otherwise) and runs gates, Sinkhorn and pass 2.
+template <int N, int DT, int MODE, int L>
+static hipError_t launch_splitk_nl(const FusedArgs &a, hipStream_t s) {
+    constexpr int V = StateVec<DT>::V;
+    const int P = colchunk_chunks(a.d, DT);
+    hipError_t e = launch_colchunk_pre<N, DT, L>(a, P, s);
     if (e != hipSuccess) return e;
     const dim3 g2((unsigned)a.T, (unsigned)((a.d + 64 * V - 1) / (64 * V)));
-    return launch_kernel(hc_finish_kernel<N, DT, MODE>, g2, dim3(64), s, a.d, N * a.d, (int)a.T, P, a.eps,
-                         a.iters, a.X, a.bias, (const float *)a.ws, a.layer_out, a.layer_in,
-                         a.coeffs, a.logits, a.X_out);
+    return launch_kernel(hc_finish_kernel<N, DT, MODE, L == 16 ? 64 : 32>, g2, dim3(64), s, a.d, N * a.d,
+                         (int)a.T, P, a.eps, a.iters, a.X, a.bias, (const float *)a.ws, a.layer_out,
+                         a.layer_in, a.coeffs, a.logits, a.X_out);
+}
+
+template <int N, int DT, int MODE>
+static hipError_t launch_splitk_n(const FusedArgs &a, hipStream_t s) {
+    return colchunk_lanes(a.d, DT) == 16 ? launch_splitk_nl<N, DT, MODE, 16>(a, s)
+                                         : launch_splitk_nl<N, DT, MODE, 32>(a, s);
 }
 
 template <int N, int DT, int MODE>
@@ -1627,12 +1606,6 @@ int tile_steps(int d, int dt) {
 
 int tile_max_steps() { return 8; }
 
-int splitk_chunks(int n, int d, int dt) {
-    const int V = dt == DT_F32 ? 4 : 8;
-    const long K = (long)n * d;
-    return (int)((K + 64 * V - 1) / (64 * V));
-}
-
 hipError_t launch_hc(const FusedArgs &a, bool fused, int path, hipStream_t s) {
     switch (a.n) {
     case 1: return dispatch_dt<1>(a.dt, fused, path, a, s);
@@ -1648,9 +1621,9 @@ hipError_t launch_hc(const FusedArgs &a, bool fused, int path, hipStream_t s) {
 template <int N, int DT, int L>
 static hipError_t launch_post_pre_nl(const FusedArgs &a, const float *coeffs_prev, hipStream_t s) {
     constexpr int V = StateVec<DT>::V;
-    const int P2 = (a.d + L * V - 1) / (L * V);
+    const int P2 = colchunk_chunks(a.d, DT);
     const dim3 g1((unsigned)((a.T + SPLITK_TOKENS - 1) / SPLITK_TOKENS), (unsigned)P2);
-    hipError_t e = launch_kernel(hc_postpre_partials_kernel<N, DT, L>, g1, dim3(64), s, a.d, (int)a.T,
+    hipError_t e = launch_kernel(hc_colchunk_partials_kernel<N, DT, L, true>, g1, dim3(64), s, a.d, (int)a.T,
                                  a.X, coeffs_prev, a.layer_out, a.W, a.X_out, a.ws);
     if (e != hipSuccess) return e;
     const dim3 g2((unsigned)a.T, (unsigned)((a.d + 64 * V - 1) / (64 * V)));
@@ -1661,18 +1634,18 @@ static hipError_t launch_post_pre_nl(const FusedArgs &a, const float *coeffs_pre
 
 template <int N, int DT>
 static hipError_t launch_post_pre_n(const FusedArgs &a, const float *coeffs_prev, hipStream_t s) {
-    return post_pre_lanes(a.d, DT) == 16 ? launch_post_pre_nl<N, DT, 16>(a, coeffs_prev, s)
+    return colchunk_lanes(a.d, DT) == 16 ? launch_post_pre_nl<N, DT, 16>(a, coeffs_prev, s)
                                          : launch_post_pre_nl<N, DT, 32>(a, coeffs_prev, s);
 }
 
-int post_pre_lanes(int d, int dt) {
+int colchunk_lanes(int d, int dt) {
     const int V = dt == DT_F32 ? 4 : 8;
     return (d + 16 * V - 1) / (16 * V) <= 64 ? 16 : 32;
 }
 
-int post_pre_chunks(int d, int dt) {
+int colchunk_chunks(int d, int dt) {
     const int V = dt == DT_F32 ? 4 : 8;
-    const int L = post_pre_lanes(d, dt);
+    const int L = colchunk_lanes(d, dt);
     return (d + L * V - 1) / (L * V);
 }
 
@@ -1706,10 +1679,9 @@ static hipError_t launch_partials_n(const FusedArgs &a, int path, hipStream_t s)
         return launch_kernel(hc_stream_partials_kernel<N, DT>,
                              dim3((unsigned)((a.T + SP_TOKENS - 1) / SP_TOKENS)), dim3(SP_WAVES * 64), s,
                              N * a.d, (int)a.T, a.X, a.W, a.logits);
-    const int P = splitk_chunks(N, a.d, DT);
-    const dim3 g1((unsigned)((a.T + SPLITK_TOKENS - 1) / SPLITK_TOKENS), (unsigned)P);
-    hipError_t e = launch_kernel(hc_partials_kernel<N, DT>, g1, dim3(64), s, a.d, (int)a.T, a.X,
-                                 a.W, a.ws);
+    const int P = colchunk_chunks(a.d, DT);
+    const hipError_t e = colchunk_lanes(a.d, DT) == 16 ? launch_colchunk_pre<N, DT, 16>(a, P, s)
+                                                       : launch_colchunk_pre<N, DT, 32>(a, P, s);
     if (e != hipSuccess) return e;
     return launch_kernel(hc_chunk_sum_kernel<N>, dim3((unsigned)a.T), dim3(64), s, (int)a.T, P,
                          (const float *)a.ws, a.logits);

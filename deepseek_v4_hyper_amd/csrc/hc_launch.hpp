@@ -33,7 +33,6 @@ int rowres_chunks(int d, int dt);
 int rowres_max_chunks(int n, int dt);
 int tile_steps(int d, int dt);
 int tile_max_steps();
-int splitk_chunks(int n, int d, int dt);
 hipError_t launch_hc(const FusedArgs &a, bool fused, int path, hipStream_t s);
 hipError_t launch_post(int n, int dt, int d, int64_t T, const void *X, const float *coeffs,
                        const void *layer_out, void *X_out, hipStream_t s);
@@ -48,8 +47,10 @@ hipError_t launch_partials(const FusedArgs &a, int path, hipStream_t s);
 // and pass 2 on the share a.X (width a.d) of a row n * d_total long.
 hipError_t launch_combine(const FusedArgs &a, int d_total, int G, const float *partials,
                           hipStream_t s);
-int post_pre_lanes(int d, int dt);   // lanes per column chunk of the one-pass step (16 or 32)
-int post_pre_chunks(int d, int dt);
+// Split-K column chunks (HC-pre, the one-pass chain step, the split over d at
+// small T): lanes per chunk (16 or 32) and the number of chunks.
+int colchunk_lanes(int d, int dt);
+int colchunk_chunks(int d, int dt);
 // Bytes of the device-resident scratch array behind ds4hc_post_pre_noalloc,
 // and its address on the current device (looked up once per device).
 constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(2) << 20;

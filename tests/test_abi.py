@@ -68,12 +68,16 @@ def test_version_and_status_strings():
 
 def test_workspace_bytes_is_pure_and_path_dependent():
     p = B.make_params(4, 4096)
-    # T up to 160 takes the split-K path: chunks * T * (m + 1) floats
-    P = (4 * 4096) // 256
+    # T up to 160 takes the split-K path: column chunks of 16 lanes x V columns of
+    # every stream (32 lanes where 16 would give more than 64 chunks), chunks * T *
+    # (m + 1) floats
+    P = 4096 // 64
     assert B.ds4hc_workspace_bytes(p, 1, B.DS4HC_F32) == P * 1 * 25 * 4
     assert B.ds4hc_workspace_bytes(p, 4, B.DS4HC_F32) == P * 4 * 25 * 4
-    Pb = (4 * 4096) // 512
+    Pb = 4096 // 128
     assert B.ds4hc_workspace_bytes(p, 4, B.DS4HC_BF16) == Pb * 4 * 25 * 4
+    assert B.ds4hc_workspace_bytes(B.make_params(4, 7168), 2, B.DS4HC_F32) == (7168 // 128) * 2 * 25 * 4
+    assert B.ds4hc_workspace_bytes(B.make_params(2, 264), 3, B.DS4HC_F32) == 5 * 3 * 9 * 4  # ragged, m = 8
     assert B.ds4hc_workspace_bytes(p, 4096, B.DS4HC_F32) == 0
     pf = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_SPLITK)
     assert B.ds4hc_workspace_bytes(pf, 4096, B.DS4HC_F32) == P * 4096 * 25 * 4
@@ -268,8 +272,9 @@ def test_partials_workspace_bytes():
     assert B.ds4hc_partials_workspace_bytes(pr, 8, B.DS4HC_F32) == 0      # unsupported -> 0
     # share rows past 2^24 columns (n * d_s) leave the streamed kernel (32-bit offsets) for split-K
     assert B.ds4hc_partials_workspace_bytes(B.make_params(4, 1 << 22), 200, B.DS4HC_F32) == 0
-    big = B.make_params(4, (1 << 22) + 8)   # bfloat16: split-K takes up to 65535 chunks of 512 columns
-    assert B.ds4hc_partials_workspace_bytes(big, 200, B.DS4HC_BF16) == (4 * ((1 << 22) + 8) + 511) // 512 * 200 * 25 * 4
+    big = B.make_params(4, (1 << 22) + 8)   # split-K: 32-lane chunks of 32 x V columns of every stream
+    assert B.ds4hc_partials_workspace_bytes(big, 200, B.DS4HC_BF16) == ((1 << 22) + 8 + 255) // 256 * 200 * 25 * 4
+    assert B.ds4hc_partials_workspace_bytes(big, 200, B.DS4HC_F32) == ((1 << 22) + 8 + 127) // 128 * 200 * 25 * 4
 
 
 @no_gpu_only
