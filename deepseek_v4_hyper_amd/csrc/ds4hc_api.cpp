@@ -19,12 +19,9 @@
 
 namespace {
 
-// Default paths by T, from a sweep of every path of ds4hc_fused on MI355X at
-// n = 4, d = 4096, fp32 (bench.py --sweep): split-K is fastest through T = 128
-// (21 us against 35 us for the tile kernel), the row-resident kernel at
-// T = 256 (30 us against 34 and 36), the tile kernel from T = 512 on.
-constexpr int64_t SPLITK_MAX_T = 160;      // T at or below which split-K is the default
-constexpr int64_t ROWRES_MAX_T = 384;      // then the row-resident kernel up to here
+// T at or below which the one-pass chain step and the split-K partials of the
+// split over d are the defaults.
+constexpr int64_t SPLITK_MAX_T = 160;
 constexpr int64_t MAX_T = int64_t(1) << 24;
 constexpr int MAX_ITERS = 1000;
 constexpr uint64_t MAX_WORK_ITEMS = 0xFFFFFFFFull;  // HSA dispatch grid size is 32-bit
@@ -86,6 +83,29 @@ struct Plan {
 // at n = 4: 141.5 us against 258 us for the VALU kernel at T = 4096, d = 4096
 // float32, and 557 us against 1333 us at T = 16384, d = 7168 bfloat16), then
 // the VALU kernel, then split-K where a row is too long for either.
+// Default path of HC-pre / fused: the cheapest by a cost model fitted to a
+// sweep of every path on MI355X (graph-replayed ds4hc_fused, n = 4, f32
+// d = 4096 and bf16 d = 7168, T = 1 .. 2048), in microseconds with K = n * d:
+//   split-K       6 + 3.3e-6 * T * K                     (swept up to T = 512)
+//   row-resident  16 + 1.6e-4 * K, + 6 for 192 < T <= 256 (one token per CU)
+//   tile          30 + 2.4e-4 * max(0, K - 16384)         (flat while T <= 1024)
+// Beyond those ranges the tile kernel where it fits. Measured points:
+// f32 d = 4096: split-K 17.6 / 20.9 / 28.8 us at T = 192 / 256 / 384 against
+// row-resident 21.8 / 26.0 / 35.3 and tile 31.5 / 31.7 / 32.5; tile from 448.
+// bf16 d = 7168: split-K 19.2 us at T = 128, row-resident 20.6 / 26.9 at
+// T = 160 / 256 (split-K 23.8 / 29.8), tile from 320-384 (35.7 - 36.1).
+int default_path(int64_t T, int64_t K, bool fits_rowres, bool fits_tile) {
+    constexpr double NONE = 1e30;
+    const double k = (double)K, t = (double)T;
+    const double splitk = T <= 512 ? 6.0 + 3.3e-6 * t * k : NONE;
+    const double rowres = fits_rowres && T <= 256 ? 16.0 + 1.6e-4 * k + (T > 192 ? 6.0 : 0.0) : NONE;
+    const double tile = fits_tile ? 30.0 + 2.4e-4 * (K > 16384 ? k - 16384.0 : 0.0) : NONE;
+    if (splitk <= rowres && splitk <= tile && splitk < NONE) return ds4hc::PATH_SPLITK;
+    if (rowres <= tile && rowres < NONE) return ds4hc::PATH_ROWRES;
+    if (fits_tile) return ds4hc::PATH_TILE;
+    return fits_rowres ? ds4hc::PATH_ROWRES : ds4hc::PATH_SPLITK;
+}
+
 // Returns UNSUPPORTED if a forced path cannot take the shape or a launch
 // would not fit.
 ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *out) {
@@ -102,12 +122,8 @@ ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *o
         path = ds4hc::PATH_TILE;
     } else if (force == DS4HC_FLAG_FORCE_SPLITK) {
         path = ds4hc::PATH_SPLITK;
-    } else if (T <= SPLITK_MAX_T) {
-        path = ds4hc::PATH_SPLITK;
     } else {
-        const bool mid = T <= ROWRES_MAX_T && fits_rowres;
-        path = mid ? ds4hc::PATH_ROWRES
-                   : fits_tile ? ds4hc::PATH_TILE : fits_rowres ? ds4hc::PATH_ROWRES : ds4hc::PATH_SPLITK;
+        path = default_path(T, (int64_t)n * d, fits_rowres, fits_tile);
     }
     Plan pl{path, 0, 0};
     if (path == ds4hc::PATH_ROWRES) {

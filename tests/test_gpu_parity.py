@@ -411,8 +411,8 @@ def _post_pre_case(seed, T, n, d, dtype):
 @pytest.mark.parametrize("T", [1, 3, 37, 200])
 def test_post_pre_equals_post_then_pre(dtype, n, d, T):
     """ds4hc_post_pre against ds4hc_post followed by ds4hc_pre (T = 1, 3, 37: the
-    one-pass split-K kernels, one or several token groups; T = 200: post, then the
-    row-resident pre on X'). The one-pass step takes column chunks of 16 lanes
+    one-pass split-K kernels, one or several token groups; T = 200: post, then
+    HC-pre on X' on its default path). The one-pass step takes column chunks of 16 lanes
     where that gives at most 64 chunks, else 32: d = 7168 fp32 and d = 8200
     (either type, with a ragged last chunk) take 32. X' must be bitwise what
     ds4hc_post writes; layer_in and coeffs are checked against the oracle's HC-pre
