@@ -100,12 +100,15 @@ typedef struct {
 
 /* Every path is deterministic already; the flag is accepted and changes nothing. */
 #define DS4HC_FLAG_DETERMINISTIC 1u
-/* Force one kernel path (all compute the same op; the default picks by T and
- * row length; forcing more than one is invalid):
+/* Force one kernel path (all compute the same op; forcing more than one is
+ * invalid). The default for HC-pre and fused is the cheapest by a cost model
+ * in T and the row length K = n * d, fitted to measured times of every path
+ * (at d = 4096 float32: split-K through T = 400, the tile kernel above):
  *   ROWRES  one token per workgroup, row kept in registers, VALU matvec;
  *   TILE    persistent, one workgroup per CU striding over tiles of four
  *           tokens, rows kept in registers, MFMA matvec;
- *   SPLITK  partials over K chunks into the workspace, then a combining kernel. */
+ *   SPLITK  partials over column chunks of every stream into the workspace,
+ *           then a combining kernel. */
 #define DS4HC_FLAG_FORCE_ROWRES 2u
 #define DS4HC_FLAG_FORCE_SPLITK 4u
 #define DS4HC_FLAG_FORCE_TILE 8u
