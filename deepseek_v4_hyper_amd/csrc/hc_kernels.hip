@@ -1001,6 +1001,7 @@ __global__ __launch_bounds__(SP_WAVES * 64) void hc_stream_partials_kernel(int K
                                                                            float *__restrict__ out) {
     constexpr int M = n_logits(N);
     constexpr int RB = (M + 15) / 16;  // 16-row blocks of W
+    static_assert((M + 1) * SP_TOKENS <= SP_WAVES * 64, "one thread per output of the final sum");
     typedef float f4_t __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
