@@ -127,9 +127,17 @@ __device__ __forceinline__ float half_get(const HalfVec<V> &h, int e) {
     return (e & 1) ? f16_hi(w) : f16_lo(w);
 }
 
+// Lane exchange by DPP control CTRL (only quad permutations and row rotations
+// are used: every lane has a valid source). bound_ctrl is set so that the
+// compiler folds the move into the instruction that consumes it (v_add_f32
+// with a DPP source operand, one instruction instead of two on the serial
+// chains of the reductions and the Sinkhorn); with every source valid it
+// changes no value.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    static_assert((CTRL >= 0x00 && CTRL <= 0xFF) || (CTRL >= 0x121 && CTRL <= 0x12F),
+                  "quad permutations and row rotations only");
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over the 64 lanes of a wavefront, entirely in the VALU: quad butterflies
@@ -164,9 +172,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 // uniform and permutation cases) are still exact. A product with the
 // reciprocal can exceed 1 by an ulp where an entry is its whole row or column
 // sum (a quotient cannot), so the result is clamped to 1; the comparison keeps
-// NaN as NaN.
+// NaN as NaN. No contraction here: fused into the next sum, a lane's own
+// product would enter it unrounded while its partners' entered rounded, and
+// the lanes of a row or column would no longer hold the same sum bits.
 template <int N>
 __device__ __forceinline__ float sinkhorn_lane_dpp(float z, int iters) {
+#pragma clang fp contract(off)
     static_assert(N == 1 || N == 2 || N == 4, "n_hc");
     if constexpr (N == 1) {
         float m = expf(z - z);

@@ -439,8 +439,8 @@ __device__ __forceinline__ void set_wave_prio(bool high, bool base) {
 // Sum over the 16 lanes of a DPP row that share lane % 4 (blocks of a row):
 // rotations by 4 and 8 lanes.
 __device__ __forceinline__ float row_sum_by4(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    v += dpp_mov<0x124>(v);  // row_ror:4
+    v += dpp_mov<0x128>(v);  // row_ror:8
     return v;
 }
 
