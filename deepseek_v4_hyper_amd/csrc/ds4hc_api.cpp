@@ -87,19 +87,22 @@ struct Plan {
 // sweep of every path on MI355X (graph-replayed ds4hc_fused, n = 4, f32
 // d = 4096 and bf16 d = 7168, T = 1 .. 2048), in microseconds with K = n * d:
 //   split-K       6 + 3.3e-6 * T * K                     (swept up to T = 512)
-//   row-resident  16 + 1.6e-4 * K, + 6 for 192 < T <= 256 (one token per CU)
-//   tile          30 + 2.4e-4 * max(0, K - 16384)         (flat while T <= 1024)
+//   row-resident  16 + 1.6e-4 * K, + 6 * (T - 192) / 64 for 192 < T <= 256
+//                 (one token per CU)
+//   tile          32.3 + 2.6e-4 * max(0, K - 16384)       (flat while T <= 1024)
 // Beyond those ranges the tile kernel where it fits. Measured points:
-// f32 d = 4096: split-K 17.6 / 20.9 / 28.8 us at T = 192 / 256 / 384 against
-// row-resident 21.8 / 26.0 / 35.3 and tile 31.5 / 31.7 / 32.5; tile from 448.
-// bf16 d = 7168: split-K 19.2 us at T = 128, row-resident 20.6 / 26.9 at
-// T = 160 / 256 (split-K 23.8 / 29.8), tile from 320-384 (35.7 - 36.1).
+// f32 d = 4096: split-K 17.6 / 20.9 / 28.0 / 30.7 us at T = 192 / 256 / 384 /
+// 448 against row-resident 21.8 / 26.0 / 34.4 / 35.7 and tile 31.5 / 31.7 /
+// 32.3 / 32.6; tile faster from T = 464 (32.5 against 33.3).
+// bf16 d = 7168: split-K 18.9 us at T = 144, row-resident 20.2 / 21.3 / 25.9
+// at T = 160 / 200 / 256 (split-K 22.7 / 25.0 / 28.8), split-K again at
+// T = 272 / 288 (29.3 / 29.7 against tile 35.7), tile from ~320 (35.8).
 int default_path(int64_t T, int64_t K, bool fits_rowres, bool fits_tile) {
     constexpr double NONE = 1e30;
     const double k = (double)K, t = (double)T;
     const double splitk = T <= 512 ? 6.0 + 3.3e-6 * t * k : NONE;
-    const double rowres = fits_rowres && T <= 256 ? 16.0 + 1.6e-4 * k + (T > 192 ? 6.0 : 0.0) : NONE;
-    const double tile = fits_tile ? 30.0 + 2.4e-4 * (K > 16384 ? k - 16384.0 : 0.0) : NONE;
+    const double rowres = fits_rowres && T <= 256 ? 16.0 + 1.6e-4 * k + (T > 192 ? 6.0 * (t - 192.0) / 64.0 : 0.0) : NONE;
+    const double tile = fits_tile ? 32.3 + 2.6e-4 * (K > 16384 ? k - 16384.0 : 0.0) : NONE;
     if (splitk <= rowres && splitk <= tile && splitk < NONE) return ds4hc::PATH_SPLITK;
     if (rowres <= tile && rowres < NONE) return ds4hc::PATH_ROWRES;
     if (fits_tile) return ds4hc::PATH_TILE;

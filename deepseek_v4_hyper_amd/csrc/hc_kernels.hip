@@ -2,23 +2,26 @@
 // MI355X (gfx950) and their host-side launchers.
 //
 // Three paths compute the same op (see ds4hc.h for its definition); the
-// library picks one by T (thresholds from a measured sweep), and flags can
-// force any of them:
+// library picks one with a cost model in T and the row length K = n*d, fitted
+// to a measured sweep (ds4hc_api.cpp: split-K up to T = 400 at float32
+// d = 4096, up to T = 150 at bfloat16 d = 7168, row-resident between 160 and
+// 256 at the latter, tile above), and flags can force any of them:
 //
-//  * tile (T > 384): a persistent MFMA kernel, one 512-thread workgroup per
+//  * tile (large T): a persistent MFMA kernel, one 512-thread workgroup per
 //    CU striding over tiles of four tokens. A tile's rows live in registers,
 //    so X is read once and X' written once; the fn matvec runs on
 //    v_mfma_f32_4x4x4_16b_f16 with W streamed from L2 through per-wave LDS
 //    rings, and the drained rings stage half of the next tile's rows.
 //
-//  * row-resident (161 <= T <= 384, or rows too long for the tile kernel):
+//  * row-resident (mid-size T where the cost model puts it, or rows too long
+//    for the tile kernel):
 //    one 256-thread workgroup per token; the token's n*d state is loaded once
 //    into registers, the RMS statistic and the m = 2n + n*n fn dot products
 //    are accumulated from it on the VALU, reduced in a fixed order, the gates
 //    and the register-resident Sinkhorn run in one wavefront, and the pre-mix
 //    and post update are computed from the same registers.
 //
-//  * split-K (T <= 160, decode and speculative verify): the fn weight (m*K
+//  * split-K (small T: decode and speculative verify): the fn weight (m*K
 //    float16, 768 KiB at d = 4096) dominates the bytes, so K is cut into
 //    chunks and many workgroups each read one chunk of W for all tokens,
 //    writing fixed-order partial sums to a caller workspace. A second kernel

@@ -103,7 +103,7 @@ typedef struct {
 /* Force one kernel path (all compute the same op; forcing more than one is
  * invalid). The default for HC-pre and fused is the cheapest by a cost model
  * in T and the row length K = n * d, fitted to measured times of every path
- * (at d = 4096 float32: split-K through T = 400, the tile kernel above):
+ * (at d = 4096 float32: split-K through T = 486, the tile kernel above):
  *   ROWRES  one token per workgroup, row kept in registers, VALU matvec;
  *   TILE    persistent, one workgroup per CU striding over tiles of four
  *           tokens, rows kept in registers, MFMA matvec;

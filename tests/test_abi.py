@@ -212,14 +212,15 @@ def post_pre(p, T=8, dt=B.DS4HC_F32, **over):
 def test_default_path_follows_the_measured_crossover():
     """HC-pre / fused pick split-K (the only path with a workspace), the row-resident
     or the tile kernel by the cost model fitted to the path sweep: split-K through
-    T = 400 at f32 d = 4096 (tile from 448); at bf16 d = 7168 split-K through T = 150,
-    then the row-resident kernel, then the tile kernel; split-K never above T = 512."""
+    T = 448 at f32 d = 4096 (tile from 512); at bf16 d = 7168 split-K through T = 144,
+    the row-resident kernel from 160 through 256 (200 and 240 included), split-K again
+    at 272 and 288, then the tile kernel; split-K never above T = 512."""
     def splitk(n, d, T, dt):
         return B.ds4hc_workspace_bytes(B.make_params(n, d), T, dt) > 0
-    assert all(splitk(4, 4096, T, B.DS4HC_F32) for T in (1, 4, 160, 192, 256, 384, 400))
-    assert not any(splitk(4, 4096, T, B.DS4HC_F32) for T in (448, 512, 1024, 4096))
-    assert all(splitk(4, 7168, T, B.DS4HC_BF16) for T in (1, 4, 128, 150))
-    assert not any(splitk(4, 7168, T, B.DS4HC_BF16) for T in (160, 256, 384, 16384))
+    assert all(splitk(4, 4096, T, B.DS4HC_F32) for T in (1, 4, 160, 192, 256, 384, 400, 448))
+    assert not any(splitk(4, 4096, T, B.DS4HC_F32) for T in (512, 1024, 4096))
+    assert all(splitk(4, 7168, T, B.DS4HC_BF16) for T in (1, 4, 128, 144, 272, 288))
+    assert not any(splitk(4, 7168, T, B.DS4HC_BF16) for T in (160, 200, 240, 256, 320, 384, 16384))
     assert splitk(4, 256, 512, B.DS4HC_F32) and not splitk(4, 256, 513, B.DS4HC_F32)
 
 
@@ -234,7 +235,7 @@ def test_post_pre_workspace_bytes():
     assert B.ds4hc_post_pre_workspace_bytes(p7, 2, B.DS4HC_BF16) == (7168 // 128) * 2 * 25 * 4
     assert B.ds4hc_post_pre_workspace_bytes(p7, 2, B.DS4HC_F32) == (7168 // 128) * 2 * 25 * 4  # 32 lanes
     assert B.ds4hc_post_pre_workspace_bytes(B.make_params(4, 256), 1, B.DS4HC_F32) == 4 * 25 * 4
-    # larger T: post, then HC-pre on its default path (split-K through T = 400 at
+    # larger T: post, then HC-pre on its default path (split-K through T = 486 at
     # d = 4096 f32, with its workspace; the tile kernel above: none)
     assert B.ds4hc_post_pre_workspace_bytes(p, 161, B.DS4HC_F32) == 64 * 161 * 25 * 4
     assert B.ds4hc_post_pre_workspace_bytes(p, 4096, B.DS4HC_F32) == 0
