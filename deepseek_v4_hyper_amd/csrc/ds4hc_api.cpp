@@ -11,6 +11,7 @@
 // device, cannot have it.)
 #include "ds4hc.h"
 
+#include <algorithm>
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
@@ -83,13 +84,16 @@ struct Plan {
 // at n = 4: 141.5 us against 258 us for the VALU kernel at T = 4096, d = 4096
 // float32, and 557 us against 1333 us at T = 16384, d = 7168 bfloat16), then
 // the VALU kernel, then split-K where a row is too long for either.
-// Default path of HC-pre / fused: the cheapest by a cost model fitted to a
-// sweep of every path on MI355X (graph-replayed ds4hc_fused, n = 4, f32
-// d = 4096 and bf16 d = 7168, T = 1 .. 2048), in microseconds with K = n * d:
-//   split-K       6 + 3.3e-6 * T * K                     (swept up to T = 512)
+// Default path of HC-pre / fused: the cheapest by a cost model fitted to
+// sweeps of every path on MI355X (graph-replayed ds4hc_fused, n = 4: f32
+// d = 4096 and bf16 d = 7168 over T = 1 .. 2048, f32 d = 256, 1024, 2048 and
+// bf16 d = 256 over T = 1 .. 256), in microseconds with K = n * d:
+//   split-K       6 + 3.3e-6 * T * K, at least 6.9 (T = 1) or 8.6 (two
+//                 kernels' latency)                      (swept up to T = 512)
 //   row-resident  16 + 1.6e-4 * K, + 6 * (T - 192) / 64 for 192 < T <= 256
 //                 (one token per CU)
-//   tile          32.3 + 2.6e-4 * max(0, K - 16384)       (flat while T <= 1024)
+//   tile          32.3 + 2.6e-4 * (K - 16384) from K = 16384, 5 + 1.65e-3 * K
+//                 below (a tile's weight stream)         (flat while T <= 1024)
 // Beyond those ranges the tile kernel where it fits. Measured points:
 // f32 d = 4096: split-K 17.6 / 20.9 / 28.0 / 30.7 us at T = 192 / 256 / 384 /
 // 448 against row-resident 21.8 / 26.0 / 34.4 / 35.7 and tile 31.5 / 31.7 /
@@ -97,12 +101,14 @@ struct Plan {
 // bf16 d = 7168: split-K 18.9 us at T = 144, row-resident 20.2 / 21.3 / 25.9
 // at T = 160 / 200 / 256 (split-K 22.7 / 25.0 / 28.8), split-K again at
 // T = 272 / 288 (29.3 / 29.7 against tile 35.7), tile from ~320 (35.8).
+// f32 d = 256: tile 6.6 / 7.2 / 7.5 us at T = 1 / 4 / 256 against split-K
+// 6.9 / 8.6 / 9.1; d = 1024: split-K 7.1 / 8.8 against tile 8.7 / 11.2.
 int default_path(int64_t T, int64_t K, bool fits_rowres, bool fits_tile) {
     constexpr double NONE = 1e30;
     const double k = (double)K, t = (double)T;
-    const double splitk = T <= 512 ? 6.0 + 3.3e-6 * t * k : NONE;
+    const double splitk = T <= 512 ? std::max(6.0 + 3.3e-6 * t * k, T == 1 ? 6.9 : 8.6) : NONE;
     const double rowres = fits_rowres && T <= 256 ? 16.0 + 1.6e-4 * k + (T > 192 ? 6.0 * (t - 192.0) / 64.0 : 0.0) : NONE;
-    const double tile = fits_tile ? 32.3 + 2.6e-4 * (K > 16384 ? k - 16384.0 : 0.0) : NONE;
+    const double tile = !fits_tile ? NONE : K >= 16384 ? 32.3 + 2.6e-4 * (k - 16384.0) : 5.0 + 1.65e-3 * k;
     if (splitk <= rowres && splitk <= tile && splitk < NONE) return ds4hc::PATH_SPLITK;
     if (rowres <= tile && rowres < NONE) return ds4hc::PATH_ROWRES;
     if (fits_tile) return ds4hc::PATH_TILE;

@@ -77,7 +77,8 @@ def test_workspace_bytes_is_pure_and_path_dependent():
     Pb = 4096 // 128
     assert B.ds4hc_workspace_bytes(p, 4, B.DS4HC_BF16) == Pb * 4 * 25 * 4
     assert B.ds4hc_workspace_bytes(B.make_params(4, 7168), 2, B.DS4HC_F32) == (7168 // 128) * 2 * 25 * 4
-    assert B.ds4hc_workspace_bytes(B.make_params(2, 264), 3, B.DS4HC_F32) == 5 * 3 * 9 * 4  # ragged, m = 8
+    ps = B.make_params(2, 264, flags=B.DS4HC_FLAG_FORCE_SPLITK)
+    assert B.ds4hc_workspace_bytes(ps, 3, B.DS4HC_F32) == 5 * 3 * 9 * 4  # ragged, m = 8
     assert B.ds4hc_workspace_bytes(p, 4096, B.DS4HC_F32) == 0
     pf = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_SPLITK)
     assert B.ds4hc_workspace_bytes(pf, 4096, B.DS4HC_F32) == P * 4096 * 25 * 4
@@ -214,14 +215,17 @@ def test_default_path_follows_the_measured_crossover():
     or the tile kernel by the cost model fitted to the path sweep: split-K through
     T = 448 at f32 d = 4096 (tile from 512); at bf16 d = 7168 split-K through T = 144,
     the row-resident kernel from 160 through 256 (200 and 240 included), split-K again
-    at 272 and 288, then the tile kernel; split-K never above T = 512."""
+    at 272 and 288, then the tile kernel; split-K never above T = 512. Short rows:
+    the tile kernel at f32 d = 256 (its weight stream is short), split-K at d = 1024."""
     def splitk(n, d, T, dt):
         return B.ds4hc_workspace_bytes(B.make_params(n, d), T, dt) > 0
     assert all(splitk(4, 4096, T, B.DS4HC_F32) for T in (1, 4, 160, 192, 256, 384, 400, 448))
     assert not any(splitk(4, 4096, T, B.DS4HC_F32) for T in (512, 1024, 4096))
     assert all(splitk(4, 7168, T, B.DS4HC_BF16) for T in (1, 4, 128, 144, 272, 288))
     assert not any(splitk(4, 7168, T, B.DS4HC_BF16) for T in (160, 200, 240, 256, 320, 384, 16384))
-    assert splitk(4, 256, 512, B.DS4HC_F32) and not splitk(4, 256, 513, B.DS4HC_F32)
+    assert not any(splitk(4, 256, T, B.DS4HC_F32) for T in (1, 4, 64, 256, 4096))
+    assert all(splitk(4, 1024, T, B.DS4HC_F32) for T in (1, 4, 64))
+    assert all(splitk(4, 2048, T, B.DS4HC_F32) for T in (1, 4, 64))
 
 
 def test_post_pre_workspace_bytes():
