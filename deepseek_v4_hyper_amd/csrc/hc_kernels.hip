@@ -3,9 +3,8 @@
 //
 // Three paths compute the same op (see ds4hc.h for its definition); the
 // library picks one with a cost model in T and the row length K = n*d, fitted
-// to a measured sweep (ds4hc_api.cpp: split-K up to T = 400 at float32
-// d = 4096, up to T = 150 at bfloat16 d = 7168, row-resident between 160 and
-// 256 at the latter, tile above), and flags can force any of them:
+// to measured sweeps of every path (default_path in ds4hc_api.cpp), and flags
+// can force any of them:
 //
 //  * tile (large T): a persistent MFMA kernel, one 512-thread workgroup per
 //    CU striding over tiles of four tokens. A tile's rows live in registers,
