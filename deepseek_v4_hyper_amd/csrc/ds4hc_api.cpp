@@ -27,8 +27,8 @@ constexpr int64_t MAX_T = int64_t(1) << 24;
 constexpr int MAX_ITERS = 1000;
 constexpr uint64_t MAX_WORK_ITEMS = 0xFFFFFFFFull;  // HSA dispatch grid size is 32-bit
 // The streamed partials kernel forms 32-bit byte offsets up to 64 * n * d_s;
-// longer share rows take split-K.
-constexpr uint64_t STREAM_MAX_K = uint64_t(1) << 24;
+// longer share rows take split-K (ds4hc::STREAM_K_MAX).
+constexpr uint64_t STREAM_MAX_K = (uint64_t)ds4hc::STREAM_K_MAX;
 constexpr uint32_t FORCE_FLAGS =
     DS4HC_FLAG_FORCE_ROWRES | DS4HC_FLAG_FORCE_TILE | DS4HC_FLAG_FORCE_SPLITK;
 constexpr uint32_t KNOWN_FLAGS = DS4HC_FLAG_DETERMINISTIC | FORCE_FLAGS;
@@ -87,26 +87,29 @@ struct Plan {
 // Default path of HC-pre / fused: the cheapest by a cost model fitted to
 // sweeps of every path on MI355X (graph-replayed ds4hc_fused, n = 4: f32
 // d = 4096 and bf16 d = 7168 over T = 1 .. 2048, f32 d = 256, 1024, 2048 and
-// bf16 d = 256 over T = 1 .. 256), in microseconds with K = n * d:
-//   split-K       6 + 3.3e-6 * T * K, at least 6.9 (T = 1) or 8.6 (two
-//                 kernels' latency)                      (swept up to T = 512)
+// bf16 d = 256 over T = 1 .. 256), in microseconds with K = n * d and sb the
+// state's bytes per element:
+//   split-K       6 + (3.9e-7 + 6.75e-7 * sb) * T * K, at least 6.9 (T = 1)
+//                 or 8.6 (two kernels' latency); fitted where it meets the
+//                 tile kernel (it is concave in T above ~300)
+//                                                        (swept up to T = 1024)
 //   row-resident  16 + 1.6e-4 * K, + 6 * (T - 192) / 64 for 192 < T <= 256
 //                 (one token per CU)
 //   tile          32.3 + 2.6e-4 * (K - 16384) from K = 16384, 5 + 1.65e-3 * K
 //                 below (a tile's weight stream)         (flat while T <= 1024)
-// Beyond those ranges the tile kernel where it fits. Measured points:
-// f32 d = 4096: split-K 17.6 / 20.9 / 28.0 / 30.7 us at T = 192 / 256 / 384 /
-// 448 against row-resident 21.8 / 26.0 / 34.4 / 35.7 and tile 31.5 / 31.7 /
-// 32.3 / 32.6; tile faster from T = 464 (32.5 against 33.3).
-// bf16 d = 7168: split-K 18.9 us at T = 144, row-resident 20.2 / 21.3 / 25.9
-// at T = 160 / 200 / 256 (split-K 22.7 / 25.0 / 28.8), split-K again at
-// T = 272 / 288 (29.3 / 29.7 against tile 35.7), tile from ~320 (35.8).
-// f32 d = 256: tile 6.6 / 7.2 / 7.5 us at T = 1 / 4 / 256 against split-K
-// 6.9 / 8.6 / 9.1; d = 1024: split-K 7.1 / 8.8 against tile 8.7 / 11.2.
-int default_path(int64_t T, int64_t K, bool fits_rowres, bool fits_tile) {
+// Beyond those ranges the tile kernel where it fits. Measured points (split-K
+// streams its partials from T = 32):
+// f32 d = 4096: split-K 12.5 / 18.9 / 29.5 / 32.0 / 43.0 us at T = 128 / 256 /
+// 448 / 512 / 768 against tile 31.4 / 32.4 / 32.5 / 32.7 / 33.4.
+// bf16 d = 7168: split-K 14.7 / 22.1 / 26.5 / 31.8 / 32.9 / 44.6 at T = 128 /
+// 256 / 320 / 448 / 512 / 768 against row-resident 19.6 / 26.0 / 34.5 / - and
+// tile 35.3 - 36.9 / 37.9.
+// f32 d = 256: tile 6.6 / 7.1 / 7.5 us at T = 1 / 4 / 256 against split-K
+// 6.8 / 8.5 / 9.2; d = 1024: split-K 7.0 / 8.8 against tile 8.6 / 10.9.
+int default_path(int64_t T, int64_t K, int sb, bool fits_rowres, bool fits_tile) {
     constexpr double NONE = 1e30;
     const double k = (double)K, t = (double)T;
-    const double splitk = T <= 512 ? std::max(6.0 + 3.3e-6 * t * k, T == 1 ? 6.9 : 8.6) : NONE;
+    const double splitk = T <= 1024 ? std::max(6.0 + (3.9e-7 + 6.75e-7 * sb) * t * k, T == 1 ? 6.9 : 8.6) : NONE;
     const double rowres = fits_rowres && T <= 256 ? 16.0 + 1.6e-4 * k + (T > 192 ? 6.0 * (t - 192.0) / 64.0 : 0.0) : NONE;
     const double tile = !fits_tile ? NONE : K >= 16384 ? 32.3 + 2.6e-4 * (k - 16384.0) : 5.0 + 1.65e-3 * k;
     if (splitk <= rowres && splitk <= tile && splitk < NONE) return ds4hc::PATH_SPLITK;
@@ -132,7 +135,7 @@ ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *o
     } else if (force == DS4HC_FLAG_FORCE_SPLITK) {
         path = ds4hc::PATH_SPLITK;
     } else {
-        path = default_path(T, (int64_t)n * d, fits_rowres, fits_tile);
+        path = default_path(T, (int64_t)n * d, state_bytes(dt), fits_rowres, fits_tile);
     }
     Plan pl{path, 0, 0};
     if (path == ds4hc::PATH_ROWRES) {
@@ -140,12 +143,14 @@ ds4hc_status make_plan(const ds4hc_params *p, int64_t T, ds4hc_dtype dt, Plan *o
     } else if (path == ds4hc::PATH_TILE) {
         // persistent grid: at most one workgroup per CU, whatever T is
     } else {
-        pl.P = ds4hc::colchunk_chunks(d, dt);
-        const uint64_t tg = (uint64_t)(T + 3) / 4;
+        // partials grid (token groups, P): 4 tokens by 64 threads per group on
+        // the column-chunk kernel, 16 by 512 on the streamed one; finish grid
+        // (T, column blocks)
+        const bool streamed = ds4hc::splitk_streams(T, (int64_t)n * d);
+        pl.P = streamed ? ds4hc::stream_chunks(T, n * d) : ds4hc::colchunk_chunks(d, dt);
+        const uint64_t tg_threads = streamed ? (uint64_t)(T + 15) / 16 * 512u : (uint64_t)(T + 3) / 4 * 64u;
         const uint64_t cb = (uint64_t)(d + 64 * vec_elems(dt) - 1) / (64 * vec_elems(dt));
-        // partials grid (token groups, P), finish grid (T, column blocks)
-        if (tg * 64u > MAX_WORK_ITEMS || pl.P > 0xFFFF || (uint64_t)T * 64u > MAX_WORK_ITEMS ||
-            cb > 0xFFFFu)
+        if (tg_threads > MAX_WORK_ITEMS || pl.P > 0xFFFF || (uint64_t)T * 64u > MAX_WORK_ITEMS || cb > 0xFFFFu)
             return DS4HC_ERR_UNSUPPORTED;
         pl.ws_bytes = (uint64_t)pl.P * (uint64_t)T * (uint64_t)(m + 1) * sizeof(float);
     }

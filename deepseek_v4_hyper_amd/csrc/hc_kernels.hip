@@ -966,11 +966,14 @@ __device__ __forceinline__ float sum_chunks(const float *__restrict__ p, size_t 
 }
 
 // ---------------------------------------------------------------------------
-// Split-over-d partials for large T, streamed: grid ceil(T / 16), 512 threads.
-// With no pass 2 the rows need not stay on chip, so a workgroup takes 16
-// tokens and streams their share rows, and the whole share weight, through
-// its CU once (the tile kernel's partials mode streams the weight once per 4
-// tokens). The flattened share row (K = n * d_s columns) is cut into k-steps
+// Streamed partials: grid (ceil(T / 16), column chunks), 512 threads. For the
+// split over d at large T one chunk holds the whole share row; split-K from
+// T = 32 takes chunks of KC columns (multiples of 256) of the row, each
+// chunk's sums to its slice of the workspace. With no pass 2 the rows need not
+// stay on chip, so a workgroup takes 16 tokens and streams their rows, and
+// its chunk of the weight, through its CU once (the tile kernel's partials
+// mode streams the weight once per 4 tokens, the column-chunk kernel once per
+// 4). The chunk (K = n * d_s columns for the split over d) is cut into k-steps
 // of 32 columns; wave w takes the w-th of eight contiguous runs of steps.
 // Lane l holds token l % 16 and columns 8 (l / 16) .. + 7 of a step: 32 bytes
 // of its token's row (16 for bfloat16) and 16 bytes of each of its W rows,
@@ -998,7 +1001,8 @@ constexpr int SP_WAVES = 8;
 constexpr int SP_BATCH = 1;  // k-steps of 32 columns per register batch (two batches)
 
 template <int N, int DT>
-__global__ __launch_bounds__(SP_WAVES * 64) void hc_stream_partials_kernel(int K, int T, const void *__restrict__ X,
+__global__ __launch_bounds__(SP_WAVES * 64) void hc_stream_partials_kernel(int K, int KC, int T,
+                                                                           const void *__restrict__ X,
                                                                            const uint16_t *__restrict__ W,
                                                                            float *__restrict__ out) {
     constexpr int M = n_logits(N);
@@ -1016,7 +1020,13 @@ __global__ __launch_bounds__(SP_WAVES * 64) void hc_stream_partials_kernel(int K
     // all of them read zeros with no branch or select.
     const __amdgpu_buffer_rsrc_t xr = make_rsrc((const char *)X + (size_t)t0 * K * SB, (uint32_t)((size_t)ntok * K * SB));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)((size_t)M * K * 2));
-    const int nsteps = (K + 31) / 32;
+    // column chunk blockIdx.y: columns [kbase, kend) of the flattened row,
+    // its sums to out[blockIdx.y][T][M + 1] (one chunk of all K columns for
+    // the split over d)
+    const int kbase = blockIdx.y * KC;
+    const int kend = min(K, kbase + KC);
+    out += (size_t)blockIdx.y * T * (M + 1);
+    const int nsteps = (kend - kbase + 31) / 32;
     const int per = (nsteps + SP_WAVES - 1) / SP_WAVES;
     const int first = wave * per;
     const int mine = max(0, min(per, nsteps - first));
@@ -1034,8 +1044,8 @@ __global__ __launch_bounds__(SP_WAVES * 64) void hc_stream_partials_kernel(int K
     auto fetch = [&](Batch &bt, int i) {
 #pragma unroll
         for (int j = 0; j < SP_BATCH; ++j) {
-            const int k = (first + i + j) * 32 + 8 * grp;
-            const bool ok = i + j < mine && k < K;
+            const int k = kbase + (first + i + j) * 32 + 8 * grp;
+            const bool ok = i + j < mine && k < kend;
             // (offsets pinned in a register: given the constant OOB_OFFSET in
             // one arm, the compiler otherwise branches between two loads)
             int xo = ok ? (tok * K + k) * SB : OOB_OFFSET;
@@ -1569,8 +1579,28 @@ static hipError_t launch_splitk_nl(const FusedArgs &a, hipStream_t s) {
                          a.layer_in, a.coeffs, a.logits, a.X_out);
 }
 
+// Split-K where splitk_streams(T, K): the streamed 16-token MFMA partials
+// over stream_chunks column chunks (the weight read once per 16 tokens instead
+// of once per 4), then the same finish kernel.
+template <int N, int DT, int MODE>
+static hipError_t launch_splitk_stream(const FusedArgs &a, hipStream_t s) {
+    constexpr int V = StateVec<DT>::V;
+    const int K = N * a.d;
+    const int P = stream_chunks(a.T, K);
+    const int KC = stream_chunk_cols(a.T, K);
+    const dim3 g1((unsigned)((a.T + SP_TOKENS - 1) / SP_TOKENS), (unsigned)P);
+    hipError_t e = launch_kernel(hc_stream_partials_kernel<N, DT>, g1, dim3(SP_WAVES * 64), s, K, KC, (int)a.T,
+                                 a.X, a.W, (float *)a.ws);
+    if (e != hipSuccess) return e;
+    const dim3 g2((unsigned)a.T, (unsigned)((a.d + 64 * V - 1) / (64 * V)));
+    return launch_kernel(hc_finish_kernel<N, DT, MODE, 64>, g2, dim3(64), s, a.d, K, (int)a.T, P, a.eps,
+                         a.iters, a.X, a.bias, (const float *)a.ws, a.layer_out, a.layer_in, a.coeffs, a.logits,
+                         a.X_out);
+}
+
 template <int N, int DT, int MODE>
 static hipError_t launch_splitk_n(const FusedArgs &a, hipStream_t s) {
+    if (splitk_streams(a.T, (int64_t)N * a.d)) return launch_splitk_stream<N, DT, MODE>(a, s);
     return colchunk_lanes(a.d, DT) == 16 ? launch_splitk_nl<N, DT, MODE, 16>(a, s)
                                          : launch_splitk_nl<N, DT, MODE, 32>(a, s);
 }
@@ -1646,6 +1676,24 @@ int colchunk_lanes(int d, int dt) {
     return (d + 16 * V - 1) / (16 * V) <= 64 ? 16 : 32;
 }
 
+// Column chunks of the streamed split-K partials: about 512 workgroups (two
+// per CU) over ceil(T / 16) token groups, each chunk a multiple of 256
+// columns (one 32-column step per wave), at most 64 chunks.
+int stream_chunk_cols(int64_t T, int K) {
+    const int64_t groups = (T + SP_TOKENS - 1) / SP_TOKENS;
+    int64_t want = (512 + groups - 1) / groups;
+    if (want < 1) want = 1;
+    if (want > 64) want = 64;
+    int64_t kc = (K + want - 1) / want;
+    kc = (kc + 255) / 256 * 256;
+    return (int)kc;
+}
+
+int stream_chunks(int64_t T, int K) {
+    const int kc = stream_chunk_cols(T, K);
+    return (K + kc - 1) / kc;
+}
+
 int colchunk_chunks(int d, int dt) {
     const int V = dt == DT_F32 ? 4 : 8;
     const int L = colchunk_lanes(d, dt);
@@ -1681,7 +1729,7 @@ static hipError_t launch_partials_n(const FusedArgs &a, int path, hipStream_t s)
     if (path == PATH_STREAM)
         return launch_kernel(hc_stream_partials_kernel<N, DT>,
                              dim3((unsigned)((a.T + SP_TOKENS - 1) / SP_TOKENS)), dim3(SP_WAVES * 64), s,
-                             N * a.d, (int)a.T, a.X, a.W, a.logits);
+                             N * a.d, N * a.d, (int)a.T, a.X, a.W, a.logits);
     const int P = colchunk_chunks(a.d, DT);
     const hipError_t e = colchunk_lanes(a.d, DT) == 16 ? launch_colchunk_pre<N, DT, 16>(a, P, s)
                                                        : launch_colchunk_pre<N, DT, 32>(a, P, s);

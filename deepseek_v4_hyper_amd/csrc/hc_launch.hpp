@@ -51,6 +51,16 @@ hipError_t launch_combine(const FusedArgs &a, int d_total, int G, const float *p
 // small T): lanes per chunk (16 or 32) and the number of chunks.
 int colchunk_lanes(int d, int dt);
 int colchunk_chunks(int d, int dt);
+// Split-K of HC-pre / fused for T >= SPLITK_STREAM_MIN_T takes the streamed
+// 16-token partials over column chunks of stream_chunk_cols(T, K) columns of
+// the flattened row (K = n * d): stream_chunks(T, K) of them.
+// Rows up to STREAM_K_MAX columns keep the streamed kernel's 32-bit offsets
+// (16 token rows of float32) in range.
+constexpr int64_t SPLITK_STREAM_MIN_T = 32;
+constexpr int64_t STREAM_K_MAX = int64_t(1) << 24;
+inline bool splitk_streams(int64_t T, int64_t K) { return T >= SPLITK_STREAM_MIN_T && K <= STREAM_K_MAX; }
+int stream_chunk_cols(int64_t T, int K);
+int stream_chunks(int64_t T, int K);
 // Bytes of the device-resident scratch array behind ds4hc_post_pre_noalloc,
 // and its address on the current device (looked up once per device).
 constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(2) << 20;

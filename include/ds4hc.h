@@ -103,12 +103,13 @@ typedef struct {
 /* Force one kernel path (all compute the same op; forcing more than one is
  * invalid). The default for HC-pre and fused is the cheapest by a cost model
  * in T and the row length K = n * d, fitted to measured times of every path
- * (at d = 4096 float32: split-K through T = 486, the tile kernel above):
+ * (at d = 4096 float32: split-K through T = 519, the tile kernel above):
  *   ROWRES  one token per workgroup, row kept in registers, VALU matvec;
  *   TILE    persistent, one workgroup per CU striding over tiles of four
  *           tokens, rows kept in registers, MFMA matvec;
- *   SPLITK  partials over column chunks of every stream into the workspace,
- *           then a combining kernel. */
+ *   SPLITK  partials over column chunks into the workspace (4 tokens per
+ *           workgroup below T = 32, 16 from T = 32), then a combining
+ *           kernel. */
 #define DS4HC_FLAG_FORCE_ROWRES 2u
 #define DS4HC_FLAG_FORCE_SPLITK 4u
 #define DS4HC_FLAG_FORCE_TILE 8u
@@ -167,8 +168,9 @@ ds4hc_status ds4hc_fused(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype, co
 
 /* Workspace bytes ds4hc_pre / ds4hc_fused need for these arguments (0 when
  * the chosen path needs none). Pure function; 0 for invalid arguments. It takes
- * the state dtype because the split-K chunk width (64 lanes x one 16-byte
- * vector) and hence the number of partial sums depend on it. */
+ * the state dtype because the path, and below T = 32 the split-K column-chunk
+ * width (16 or 32 lanes x one 16-byte vector) and hence the number of partial
+ * sums, depend on it. */
 size_t ds4hc_workspace_bytes(const ds4hc_params *p, int64_t T, ds4hc_dtype dtype);
 
 /*

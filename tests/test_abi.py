@@ -80,8 +80,16 @@ def test_workspace_bytes_is_pure_and_path_dependent():
     ps = B.make_params(2, 264, flags=B.DS4HC_FLAG_FORCE_SPLITK)
     assert B.ds4hc_workspace_bytes(ps, 3, B.DS4HC_F32) == 5 * 3 * 9 * 4  # ragged, m = 8
     assert B.ds4hc_workspace_bytes(p, 4096, B.DS4HC_F32) == 0
+    # from T = 32 split-K takes the streamed 16-token partials over column chunks
+    # (multiples of 256 columns of the flattened row, about 512 workgroups, at
+    # most 64 chunks): 64 chunks of 256 at T = 32, 16 of 1024 at T = 448, 2 of
+    # 8192 at T = 4096
     pf = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_SPLITK)
-    assert B.ds4hc_workspace_bytes(pf, 4096, B.DS4HC_F32) == P * 4096 * 25 * 4
+    assert B.ds4hc_workspace_bytes(pf, 31, B.DS4HC_F32) == P * 31 * 25 * 4
+    assert B.ds4hc_workspace_bytes(pf, 32, B.DS4HC_F32) == 64 * 32 * 25 * 4
+    assert B.ds4hc_workspace_bytes(pf, 448, B.DS4HC_F32) == 16 * 448 * 25 * 4
+    assert B.ds4hc_workspace_bytes(pf, 4096, B.DS4HC_F32) == 2 * 4096 * 25 * 4
+    assert B.ds4hc_workspace_bytes(ps, 64, B.DS4HC_F32) == 3 * 64 * 9 * 4  # K = 528: 256, 256, 16
     pr = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_ROWRES)
     assert B.ds4hc_workspace_bytes(pr, 1, B.DS4HC_F32) == 0
     # invalid arguments give 0
@@ -212,17 +220,16 @@ def post_pre(p, T=8, dt=B.DS4HC_F32, **over):
 
 def test_default_path_follows_the_measured_crossover():
     """HC-pre / fused pick split-K (the only path with a workspace), the row-resident
-    or the tile kernel by the cost model fitted to the path sweep: split-K through
-    T = 448 at f32 d = 4096 (tile from 512); at bf16 d = 7168 split-K through T = 144,
-    the row-resident kernel from 160 through 256 (200 and 240 included), split-K again
-    at 272 and 288, then the tile kernel; split-K never above T = 512. Short rows:
-    the tile kernel at f32 d = 256 (its weight stream is short), split-K at d = 1024."""
+    or the tile kernel by the cost model fitted to the path sweeps: split-K through
+    T = 519 at f32 d = 4096 (tile from 520) and through T = 591 at bf16 d = 7168
+    (split-K streams its partials from T = 32); short rows: the tile kernel at
+    d = 256, split-K at d = 1024 and 2048 for small T."""
     def splitk(n, d, T, dt):
         return B.ds4hc_workspace_bytes(B.make_params(n, d), T, dt) > 0
-    assert all(splitk(4, 4096, T, B.DS4HC_F32) for T in (1, 4, 160, 192, 256, 384, 400, 448))
-    assert not any(splitk(4, 4096, T, B.DS4HC_F32) for T in (512, 1024, 4096))
-    assert all(splitk(4, 7168, T, B.DS4HC_BF16) for T in (1, 4, 128, 144, 272, 288))
-    assert not any(splitk(4, 7168, T, B.DS4HC_BF16) for T in (160, 200, 240, 256, 320, 384, 16384))
+    assert all(splitk(4, 4096, T, B.DS4HC_F32) for T in (1, 4, 160, 192, 256, 384, 448, 512))
+    assert not any(splitk(4, 4096, T, B.DS4HC_F32) for T in (520, 768, 1024, 4096))
+    assert all(splitk(4, 7168, T, B.DS4HC_BF16) for T in (1, 4, 128, 200, 256, 320, 448, 512))
+    assert not any(splitk(4, 7168, T, B.DS4HC_BF16) for T in (600, 768, 16384))
     assert not any(splitk(4, 256, T, B.DS4HC_F32) for T in (1, 4, 64, 256, 4096))
     assert all(splitk(4, 1024, T, B.DS4HC_F32) for T in (1, 4, 64))
     assert all(splitk(4, 2048, T, B.DS4HC_F32) for T in (1, 4, 64))
@@ -239,9 +246,9 @@ def test_post_pre_workspace_bytes():
     assert B.ds4hc_post_pre_workspace_bytes(p7, 2, B.DS4HC_BF16) == (7168 // 128) * 2 * 25 * 4
     assert B.ds4hc_post_pre_workspace_bytes(p7, 2, B.DS4HC_F32) == (7168 // 128) * 2 * 25 * 4  # 32 lanes
     assert B.ds4hc_post_pre_workspace_bytes(B.make_params(4, 256), 1, B.DS4HC_F32) == 4 * 25 * 4
-    # larger T: post, then HC-pre on its default path (split-K through T = 486 at
+    # larger T: post, then HC-pre on its default path (split-K through T = 519 at
     # d = 4096 f32, with its workspace; the tile kernel above: none)
-    assert B.ds4hc_post_pre_workspace_bytes(p, 161, B.DS4HC_F32) == 64 * 161 * 25 * 4
+    assert B.ds4hc_post_pre_workspace_bytes(p, 161, B.DS4HC_F32) == 32 * 161 * 25 * 4  # streamed, 512 columns
     assert B.ds4hc_post_pre_workspace_bytes(p, 4096, B.DS4HC_F32) == 0
     pf = B.make_params(4, 4096, flags=B.DS4HC_FLAG_FORCE_SPLITK)
     assert B.ds4hc_post_pre_workspace_bytes(pf, 4096, B.DS4HC_F32) == 64 * 4096 * 25 * 4
