@@ -113,6 +113,22 @@ def test_shapes(dtype, n, d, path):
     check_full(case, run_fused(case, FLAGS[path]), f"n={n} d={d} {dtype}/{path}")
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("n,d", [(1, 8), (1, 1032), (2, 264), (4, 8), (4, 2056), (4, 16384)])
+@pytest.mark.parametrize("T", [37, 300])
+def test_shapes_streamed_splitk(dtype, n, d, T):
+    """Split-K from T = 32 takes the streamed 16-token partials over column chunks
+    (multiples of 256 columns of the flattened row, the last one ragged where K is
+    not a multiple): a ragged last token group (T = 37) and a few dozen chunks
+    (T = 300), against the oracle."""
+    case = wl.make_random(70 + n + d + T, T, n, d, dtype)
+    got = run_fused(case, FLAGS["splitk"])
+    check_full(case, got, f"streamed split-K T={T} n={n} d={d} {dtype}")
+    again = run_fused(case, FLAGS["splitk"])
+    for a, b in zip(got, again):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), "repeat differs"
+
+
 # ------------------------------------------------------------------ persistent tile grid
 
 def _cu_count():
