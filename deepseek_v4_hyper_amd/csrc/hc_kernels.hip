@@ -1016,8 +1016,8 @@ __global__ __launch_bounds__(SP_WAVES * 64) void hc_stream_partials_kernel(int K
     const int ntok = min(SP_TOKENS, T - t0);
     constexpr int SB = DT == DT_F32 ? 4 : 2;
     // Buffer loads: tokens past T (past this group's rows) and W rows past M
-    // lie past their descriptor's end, and columns past K take OOB_OFFSET, so
-    // all of them read zeros with no branch or select.
+    // lie past their descriptor's end, and columns past the chunk's end take
+    // OOB_OFFSET, so all of them read zeros with no branch or select.
     const __amdgpu_buffer_rsrc_t xr = make_rsrc((const char *)X + (size_t)t0 * K * SB, (uint32_t)((size_t)ntok * K * SB));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)((size_t)M * K * 2));
     // column chunk blockIdx.y: columns [kbase, kend) of the flattened row,
